@@ -1,0 +1,120 @@
+"""ctypes binding of libfa.so: one Python function per C entry point.
+
+Argument marshalling only. Pointers are passed as Python ints (device
+addresses, e.g. ``tensor.data_ptr()``), the stream as an int
+(``torch.cuda.current_stream().cuda_stream``). Each function returns the
+C status code; :func:`check` turns a nonzero code into :class:`FaError`.
+The library must be built (``python -m exact_io_aware_69_amd.build``);
+loading fails loudly otherwise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/fa.h
+SIGNATURES = {
+    "fa_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
+    "fa_fwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]),
+    "fa_bwd_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
+    "fa_tile_config": (_i, [_i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "fa_fwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p]),
+    "fa_bwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz,
+                                 _p, _p, _p]),
+    "fa_status_str": (ctypes.c_char_p, [_i]),
+}
+
+FA_OK = 0
+STATUS = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED_D", -4: "FA_ERR_SCALE",
+    -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_MASK", -7: "FA_ERR_HIP", -8: "FA_ERR_ALIGN",
+}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libfa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with `python -m exact_io_aware_69_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), scale, stream)
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, stream):
+    return lib().fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, stream)
+
+
+def fa_bwd_workspace_size(B, H, N, d):
+    """Returns (status, bytes)."""
+    out = _sz(0)
+    st = lib().fa_bwd_workspace_size(B, H, N, d, ctypes.byref(out))
+    return st, out.value
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream):
+    return lib().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale, workspace,
+                        workspace_bytes, stream)
+
+
+def fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, workspace,
+                       workspace_bytes, stream):
+    return lib().fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale,
+                                    block_mask, workspace, workspace_bytes, stream)
+
+
+def fa_tile_config(pass_, d):
+    """Returns (status, bm, bn)."""
+    bm, bn = _i(0), _i(0)
+    st = lib().fa_tile_config(pass_, d, ctypes.byref(bm), ctypes.byref(bn))
+    return st, bm.value, bn.value
+
+
+def fa_fwd_debug_visits(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, visited, stream):
+    return lib().fa_fwd_debug_visits(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, visited,
+                                     stream)
+
+
+def fa_bwd_debug_visits(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, workspace,
+                        workspace_bytes, visited_kv, visited_q, stream):
+    return lib().fa_bwd_debug_visits(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale,
+                                     block_mask, workspace, workspace_bytes, visited_kv, visited_q, stream)
+
+
+def fa_status_str(status: int) -> str:
+    try:
+        return lib().fa_status_str(status).decode()
+    except ImportError:
+        return STATUS.get(status, "unknown")

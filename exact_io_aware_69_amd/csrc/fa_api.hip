@@ -1,0 +1,177 @@
+// C ABI of libfa.so: argument validation, launch geometry and status codes.
+// The declarations and the contract of every entry point are in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_params.h"
+
+namespace fa {
+hipError_t launch_fwd(const FwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st);
+hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st);
+}  // namespace fa
+
+namespace {
+
+// Largest supported sizes: every row index fits an int with room to spare
+// and B*H*N*d elements fit comfortably in 64-bit offsets.
+constexpr long long kMaxN = 1LL << 24;
+constexpr long long kMaxElems = 1LL << 40;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, float scale) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  if ((long long)B * H * N * d > kMaxElems) return FA_ERR_SHAPE;
+  if ((long long)B * H * ((N + 63) / 64) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+size_t workspace_bytes_for(int B, int H, int N) {
+  const size_t rows = (size_t)B * H * N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (sparse && !mask) return FA_ERR_MASK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.mask = mask;
+  p.visited = visited;
+  p.H = H;
+  p.N = N;
+  p.n_qt = (N + fa::FWD_BM - 1) / fa::FWD_BM;
+  p.n_kt = (N + fa::FWD_BN - 1) / fa::FWD_BN;
+  p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
+  p.c = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_fwd(p, B * H, d, causal != 0, sparse, visited != nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+             void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+             const uint8_t* mask, bool sparse, void* workspace, size_t workspace_bytes, uint8_t* visited_kv,
+             uint8_t* visited_q, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (sparse && !mask) return FA_ERR_MASK;
+  if (!workspace || workspace_bytes < workspace_bytes_for(B, H, N)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  if ((visited_kv == nullptr) != (visited_q == nullptr)) return FA_ERR_NULL;
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.lse = lse;
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.Dvec = static_cast<float*>(workspace);
+  p.mask = mask;
+  p.visited_kv = visited_kv;
+  p.visited_q = visited_q;
+  p.H = H;
+  p.N = N;
+  p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
+  p.c = scale * 1.4426950408889634f;
+  p.scale = scale;
+  hipError_t e = fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
+           float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, nullptr, false, nullptr, stream);
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                       int causal, float scale, const uint8_t* block_mask, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, true, nullptr, stream);
+}
+
+int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, 1.0f);
+  if (st != FA_OK) return st;
+  *bytes = workspace_bytes_for(B, H, N);
+  return FA_OK;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, nullptr, false, workspace,
+                  workspace_bytes, nullptr, nullptr, stream);
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                       const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, true, workspace,
+                  workspace_bytes, nullptr, nullptr, stream);
+}
+
+int fa_tile_config(int pass, int d, int* bm, int* bn) {
+  if (!bm || !bn) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  switch (pass) {
+    case 0: *bm = fa::FWD_BM; *bn = fa::FWD_BN; return FA_OK;
+    case 1: *bm = fa::BWD_KV_BM; *bn = fa::BWD_KV_BN; return FA_OK;
+    case 2: *bm = fa::BWD_Q_BM; *bn = fa::BWD_Q_BN; return FA_OK;
+    default: return FA_ERR_SHAPE;
+  }
+}
+
+int fa_fwd_debug_visits(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                        int causal, float scale, const uint8_t* block_mask, uint8_t* visited, void* stream) {
+  if (!visited) return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, block_mask != nullptr, visited, stream);
+}
+
+int fa_bwd_debug_visits(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                        void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                        const uint8_t* block_mask, void* workspace, size_t workspace_bytes, uint8_t* visited_kv,
+                        uint8_t* visited_q, void* stream) {
+  if (!visited_kv || !visited_q) return FA_ERR_NULL;
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, block_mask != nullptr,
+                  workspace, workspace_bytes, visited_kv, visited_q, stream);
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N out of range";
+    case FA_ERR_UNSUPPORTED_D: return "FA_ERR_UNSUPPORTED_D: head dimension must be 64 or 128";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA_ERR_MASK: return "FA_ERR_MASK: block-sparse call without a block mask";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: device pointers must be 16-byte aligned";
+    default: return "unknown fa status";
+  }
+}
+
+}  // extern "C"

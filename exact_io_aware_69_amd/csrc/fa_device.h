@@ -1,0 +1,115 @@
+// Device-side building blocks for the gfx950 attention kernels.
+//
+// Matrix-core conventions used throughout (CDNA4 v_mfma_f32_32x32x16_bf16,
+// checked on the hardware):
+//   * A operand (32 x 16, M x K): lane l holds row m = l % 32 and one half of
+//     K (8 bf16) selected by l / 32. B operand (16 x 32): lane l holds column
+//     n = l % 32 and the same half of K. Which 8 of the 16 K indices a half
+//     carries is free, as long as A and B agree, so every kernel states its
+//     own "slot -> index" map.
+//   * C/D (32 x 32 fp32, 16 values per lane): lane l, value r holds row
+//     8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+//   * ds_read_tr16_b64 (16-lane groups): if source lane j of a group points
+//     at element [k0 + j/4][n0 + 4*(j%4)] of a row-major bf16 matrix, lane i
+//     of the group receives [k0 + r][n0 + i] for r = 0..3, i.e. four
+//     consecutive rows of column n0 + i. This is how a row-major [key][d]
+//     tile in LDS becomes a K-contiguous MFMA operand without a transpose
+//     pass.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a per-lane value with the lane 32 apart (same MFMA column).
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16-byte global load / store of bf16 data.
+__device__ __forceinline__ u32x4 ld_global16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(FA_LDS uint8_t* base, uint32_t off, const u32x4& v) {
+  *reinterpret_cast<FA_LDS u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ bf16x8 ld_lds16(const FA_LDS uint8_t* base, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const FA_LDS u32x4*>(base + off));
+}
+// Transposing 8-byte LDS read (see the header comment).
+__device__ __forceinline__ s16x4 ld_lds_tr(const FA_LDS uint8_t* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + off));
+}
+__device__ __forceinline__ bf16x8 join_tr(const s16x4& lo, const s16x4& hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 t = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, t);
+}
+
+// Round eight fp32 values to bf16 (nearest-even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                            float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+// Four fp32 -> four bf16 packed in 8 bytes.
+__device__ __forceinline__ u32x2 pack4_bf16(float a0, float a1, float a2, float a3) {
+  bf16x4 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Logical workgroup index such that consecutive logical indices land on the
+// same XCD: the dispatcher hands consecutive hardware ids to XCDs round
+// robin, so hardware id i runs on XCD i % 8.
+__device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd, slot = bid / kXcd;
+  const int per = nwg / kXcd, rem = nwg % kXcd;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Byte offset of element (row, col) of a [rows][D] bf16 tile in LDS whose
+// 16-byte chunks are XOR-swizzled per row. The swizzle value runs through
+// all D/8 chunk indices over D/8 consecutive rows (row-wise operand reads by
+// 32 consecutive rows spread over the banks) and moves rows r..r+3 into
+// different 64-byte groups (the transposing reads touch 4 rows x 64 bytes
+// per 16 lanes).
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int row, int col) {
+  constexpr int CH = D / 8, G = CH / 4;
+  const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
+  return (uint32_t)(row * D * 2 + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1));
+}
+
+}  // namespace fa

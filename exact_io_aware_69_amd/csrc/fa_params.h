@@ -1,0 +1,57 @@
+// Kernel argument blocks and tile sizes shared by the host launcher and the
+// gfx950 kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Forward: 4 waves per workgroup, 32 query rows per wave (the waves split
+// the query rows of the tile, never the keys), key/value tiles of FWD_BN rows.
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+// Backward dK/dV kernel: a workgroup owns BWD_KV_BN keys (32 per wave) and
+// streams query tiles of BWD_KV_BM rows.
+constexpr int BWD_KV_BN = 128;
+constexpr int BWD_KV_BM = 64;
+// Backward dQ kernel: a workgroup owns BWD_Q_BM queries (32 per wave) and
+// streams key tiles of BWD_Q_BN rows.
+constexpr int BWD_Q_BM = 128;
+constexpr int BWD_Q_BN = 64;
+// Block-sparse masks are given at this granularity.
+constexpr int MASK_BLOCK = 128;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const uint8_t* mask;  // [H][nb][nb] or nullptr
+  uint8_t* visited;     // debug map [B*H][n_qt][n_kt] or nullptr
+  int H, N;
+  int n_qt, n_kt, nb;
+  float c;  // scale * log2(e)
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dO;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* Dvec;  // workspace: rowsum(dO * O), [B*H*N]
+  const uint8_t* mask;
+  uint8_t* visited_kv;  // [B*H][n_kt1][n_qt1] or nullptr
+  uint8_t* visited_q;   // [B*H][n_qt2][n_kt2] or nullptr
+  int H, N;
+  int nb;
+  float c;      // scale * log2(e)
+  float scale;  // scale, applied to dQ and dK
+};
+
+}  // namespace fa

@@ -1,0 +1,135 @@
+/*
+ * fa.h -- C ABI of the exact, IO-aware attention library (libfa.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed
+ *   Exact scaled-dot-product attention and its gradient, never writing the
+ *   N x N score matrix to device memory:
+ *     S = (Q K^T) * scale, masked entries -inf, P = softmax_row(S), O = P V,
+ *     lse_i = ln sum_j exp(S_ij).
+ *   The pages this follows: "[Paper Review] FlashAttention-2: Faster
+ *   Attention with Better Parallelism and Work Partitioning" (nubint.ai;
+ *   Abstract, "Proposed method") for exactness, the online-softmax tiling,
+ *   parallelism over sequence length and causal block skipping; and
+ *   "Researchers at Stanford University Propose FlashAttention: Fast and
+ *   Memory-Efficient Exact Attention with IO-Awareness" for keeping the
+ *   attention matrix out of HBM, saving the softmax normalisation statistic
+ *   (lse) in the forward and recomputing attention on chip in the backward,
+ *   and block-sparse attention.
+ *
+ * Conventions shared by every entry point
+ *   - q, k, v, o, dO, dq, dk, dv: device pointers to bfloat16 bit patterns
+ *     (uint16_t), contiguous [B][H][N][d] (d fastest). d must be 64 or 128.
+ *     Device pointers must be 16-byte aligned.
+ *   - lse: device pointer, float32 [B][H][N], natural-log logsumexp of the
+ *     scaled, masked score row; -inf for a row that sees no key.
+ *   - One sequence length N for queries and keys. causal != 0 makes key j
+ *     visible from query i only when j <= i.
+ *   - scale: finite and > 0 (callers normally pass 1/sqrt(d)).
+ *   - block_mask: device pointer, uint8 [H][nb][nb] with nb = ceil(N/128);
+ *     nonzero keeps the 128 x 128 block (query block, key block), shared by
+ *     every batch entry. With causal, a pair must pass both.
+ *   - stream: a hipStream_t (e.g. torch.cuda.current_stream().cuda_stream),
+ *     or NULL for the default stream. Work is only enqueued; nothing waits
+ *     on the host. Outputs must not alias inputs.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     backward workspace. The library keeps no device memory and no global
+ *     state between calls.
+ *   - Errors: every entry point returns FA_OK (0) or a negative fa_status.
+ *     Argument checks run before anything is enqueued; a failed launch is
+ *     reported as FA_ERR_HIP. Faults during execution surface at the
+ *     caller's next synchronisation of the stream.
+ *   - Output rounding: o, dq, dk, dv are rounded to bfloat16 to nearest-even
+ *     from float32 accumulators.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,           /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,          /* B, H or N < 1, or B*H*N*d too large */
+    FA_ERR_UNSUPPORTED_D = -3,  /* d not in {64, 128} */
+    FA_ERR_SCALE = -4,          /* scale not finite or <= 0 */
+    FA_ERR_WORKSPACE = -5,      /* backward workspace missing or too small */
+    FA_ERR_MASK = -6,           /* block_mask NULL in a block-sparse call */
+    FA_ERR_HIP = -7,            /* a HIP launch or runtime call failed */
+    FA_ERR_ALIGN = -8           /* a pointer is not 16-byte aligned */
+} fa_status;
+
+/* Forward. Writes o [B][H][N][d] (bf16) and lse [B][H][N] (fp32).
+ * One workgroup per (batch, head, query tile); key/value tiles are streamed
+ * through LDS with an online softmax (FlashAttention-2 review, "Proposed
+ * method"; Stanford FlashAttention summary, tiling and incremental softmax). */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/* Forward with a 128 x 128 block mask; masked blocks are skipped entirely
+ * (Stanford FlashAttention summary, block-sparse FlashAttention). */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale,
+                       const uint8_t* block_mask, void* stream);
+
+/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need:
+ * float32 D = rowsum(dO * O) for every row, O(B*H*N) -- never O(N^2). */
+int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
+
+/* Backward. Inputs: q, k, v, the forward's o and lse, and the upstream
+ * gradient dO. Writes dq, dk, dv (bf16, [B][H][N][d]). Attention
+ * probabilities are recomputed on chip from lse (Stanford FlashAttention
+ * summary, recomputation in the backward pass). Three kernels on `stream`:
+ * D = rowsum(dO*O) into the workspace; dK/dV parallel over key tiles;
+ * dQ parallel over query tiles. Deterministic (no atomics). */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward with a 128 x 128 block mask (same convention as the forward). */
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, int causal, float scale,
+                       const uint8_t* block_mask,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tile sizes the kernels use, so a caller can size the visit maps below.
+ * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel.
+ * bm = query rows per tile, bn = key rows per tile. */
+int fa_tile_config(int pass, int d, int* bm, int* bn);
+
+/* Debug forward: same computation as fa_fwd_blocksparse (block_mask may be
+ * NULL for dense) and additionally writes visited, uint8
+ * [B][H][ceil(N/bm)][ceil(N/bn)] (pass 0 tile sizes): 1 where the kernel
+ * processed the (query tile, key tile) pair, 0 where it skipped it. The
+ * caller zeroes `visited` before the call. */
+int fa_fwd_debug_visits(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, int causal, float scale,
+                        const uint8_t* block_mask, uint8_t* visited, void* stream);
+
+/* Debug backward: same computation as fa_bwd_blocksparse (block_mask may be
+ * NULL) and writes visited_kv, uint8 [B][H][ceil(N/bn1)][ceil(N/bm1)] (pass 1
+ * tile sizes, key tile major) from the dK/dV kernel and visited_q, uint8
+ * [B][H][ceil(N/bm2)][ceil(N/bn2)] (pass 2 tile sizes) from the dQ kernel.
+ * The caller zeroes both maps. */
+int fa_bwd_debug_visits(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale,
+                        const uint8_t* block_mask,
+                        void* workspace, size_t workspace_bytes,
+                        uint8_t* visited_kv, uint8_t* visited_q, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -9,3 +9,19 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def _ensure_library():
+    """Build libfa.so only when nothing is built (a stale library is the
+    caller's business: run ``python -m exact_io_aware_69_amd.build``)."""
+    from exact_io_aware_69_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_io_aware_69_amd import build
+        build.build()
+
+
+def pytest_sessionstart(session):
+    try:
+        _ensure_library()
+    except Exception as e:  # reported by the tests that need the library
+        print(f"[conftest] libfa.so could not be built: {e}")
