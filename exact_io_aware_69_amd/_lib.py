@@ -26,6 +26,7 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
+    "fa_bwd_stage": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
     "fa_tile_config": (_i, [_i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "fa_fwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p]),
     "fa_bwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz,
@@ -93,6 +94,12 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scal
                        workspace_bytes, stream):
     return lib().fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale,
                                     block_mask, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, workspace,
+                 workspace_bytes, stream):
+    return lib().fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale, block_mask,
+                              workspace, workspace_bytes, stream)
 
 
 def fa_tile_config(pass_, d):

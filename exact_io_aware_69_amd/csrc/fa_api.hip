@@ -10,7 +10,8 @@
 
 namespace fa {
 hipError_t launch_fwd(const FwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st);
-hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st);
+hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
+                      hipStream_t st);
 }  // namespace fa
 
 namespace {
@@ -64,7 +65,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
              void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
              const uint8_t* mask, bool sparse, void* workspace, size_t workspace_bytes, uint8_t* visited_kv,
-             uint8_t* visited_q, void* stream) {
+             uint8_t* visited_q, int stages, void* stream) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale);
   if (st != FA_OK) return st;
@@ -93,7 +94,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
-  hipError_t e = fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, (hipStream_t)stream);
+  hipError_t e =
+      fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, stages, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -123,14 +125,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
            size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, nullptr, false, workspace,
-                  workspace_bytes, nullptr, nullptr, stream);
+                  workspace_bytes, nullptr, nullptr, 7, stream);
 }
 
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                        void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
                        const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, true, workspace,
-                  workspace_bytes, nullptr, nullptr, stream);
+                  workspace_bytes, nullptr, nullptr, 7, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                 const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 2) return FA_ERR_SHAPE;
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, block_mask != nullptr,
+                  workspace, workspace_bytes, nullptr, nullptr, 1 << stage, stream);
 }
 
 int fa_tile_config(int pass, int d, int* bm, int* bn) {
@@ -156,7 +166,7 @@ int fa_bwd_debug_visits(const void* q, const void* k, const void* v, const void*
                         uint8_t* visited_q, void* stream) {
   if (!visited_kv || !visited_q) return FA_ERR_NULL;
   return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, block_mask != nullptr,
-                  workspace, workspace_bytes, visited_kv, visited_q, stream);
+                  workspace, workspace_bytes, visited_kv, visited_q, 7, stream);
 }
 
 const char* fa_status_str(int status) {

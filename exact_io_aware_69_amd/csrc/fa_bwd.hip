@@ -427,37 +427,48 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------ launchers
+// stages: bit 0 = D preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
-hipError_t launch_bwd_t(const BwdParams& p, int BH, hipStream_t st) {
-  const size_t rows = (size_t)BH * p.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
-                     p.dO, p.Dvec, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_kt1 = (p.N + BWD_KV_BN - 1) / BWD_KV_BN;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_kt1)), dim3(256), 0, st,
-                     p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st, p);
-  return hipGetLastError();
+hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) {
+  if (stages & 1) {
+    const size_t rows = (size_t)BH * p.N;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
+                       p.dO, p.Dvec, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
+    const int n_kt1 = (p.N + BWD_KV_BN - 1) / BWD_KV_BN;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_kt1)), dim3(256), 0,
+                       st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 4) {
+    const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st,
+                       p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, int BH, bool causal, bool sparse, bool debug, hipStream_t st) {
+hipError_t launch_bwd_d(const BwdParams& p, int BH, bool causal, bool sparse, bool debug, int stages, hipStream_t st) {
   if (debug) {
-    if (causal) return sparse ? launch_bwd_t<D, true, true, true>(p, BH, st) : launch_bwd_t<D, true, false, true>(p, BH, st);
-    return sparse ? launch_bwd_t<D, false, true, true>(p, BH, st) : launch_bwd_t<D, false, false, true>(p, BH, st);
+    if (causal) return sparse ? launch_bwd_t<D, true, true, true>(p, BH, stages, st) : launch_bwd_t<D, true, false, true>(p, BH, stages, st);
+    return sparse ? launch_bwd_t<D, false, true, true>(p, BH, stages, st) : launch_bwd_t<D, false, false, true>(p, BH, stages, st);
   }
-  if (causal) return sparse ? launch_bwd_t<D, true, true, false>(p, BH, st) : launch_bwd_t<D, true, false, false>(p, BH, st);
-  return sparse ? launch_bwd_t<D, false, true, false>(p, BH, st) : launch_bwd_t<D, false, false, false>(p, BH, st);
+  if (causal) return sparse ? launch_bwd_t<D, true, true, false>(p, BH, stages, st) : launch_bwd_t<D, true, false, false>(p, BH, stages, st);
+  return sparse ? launch_bwd_t<D, false, true, false>(p, BH, stages, st) : launch_bwd_t<D, false, false, false>(p, BH, stages, st);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st) {
-  return d == 64 ? launch_bwd_d<64>(p, BH, causal, sparse, debug, st)
-                 : launch_bwd_d<128>(p, BH, causal, sparse, debug, st);
+hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
+                      hipStream_t st) {
+  return d == 64 ? launch_bwd_d<64>(p, BH, causal, sparse, debug, stages, st)
+                 : launch_bwd_d<128>(p, BH, causal, sparse, debug, stages, st);
 }
 
 }  // namespace fa

@@ -99,6 +99,19 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                        const uint8_t* block_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* One backward kernel alone, so a caller can time or overlap them; fa_bwd
+ * (fa_bwd_blocksparse when block_mask != NULL) is exactly stages 0, 1, 2
+ * enqueued in that order on one stream. stage 0: D = rowsum(dO * O) into
+ * the workspace (reads o, dO); stage 1: dK and dV (reads q, k, v, lse, dO
+ * and the workspace written by stage 0); stage 2: dQ (same inputs). Every
+ * pointer argument is validated as in fa_bwd whatever the stage. A stage
+ * outside 0..2 returns FA_ERR_SHAPE. */
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, int causal, float scale,
+                 const uint8_t* block_mask,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Tile sizes the kernels use, so a caller can size the visit maps below.
  * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel.
  * bm = query rows per tile, bn = key rows per tile. */
