@@ -99,6 +99,14 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane l
+// of the wave writes bytes [16*l, 16*l + 16) after `lds_wave_base`, which must
+// be the same for every lane. Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, FA_LDS uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Byte offset of element (row, col) of a [rows][D] bf16 tile in LDS whose
 // 16-byte chunks are XOR-swizzled per row. The swizzle value runs through
 // all D/8 chunk indices over D/8 consecutive rows (row-wise operand reads by

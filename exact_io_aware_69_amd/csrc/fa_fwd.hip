@@ -13,47 +13,89 @@
 //     (rows are split between waves, keys are not, so no cross-wave
 //     reduction is needed).
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: lane l then holds query l % 32 and 16 keys,
-//     so the row max / row sum are an in-lane reduction plus one
-//     permlane32 swap, and the per-query rescale factor is a per-lane
-//     scalar.
+//     v_mfma_f32_32x32x16_bf16: lane l then holds query l % 32 and 16 keys
+//     per 32-key block, so the row max / row sum are an in-lane reduction
+//     plus one permlane32 swap, and the per-query rescale factor is a
+//     per-lane scalar.
 //   * The fp32 probabilities are rounded to bf16 in registers and used
 //     directly as the B operand of O^T += V^T P^T; V^T comes out of the
 //     row-major LDS tile with ds_read_tr16_b64.
-//   * K/V tiles are double-buffered in LDS (one barrier per tile); the
-//     next tile's global loads are in flight while the current one is
-//     consumed.
+//   * K/V tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no
+//     register staging), two LDS stages each, one barrier per tile: the next
+//     tile's copy is in flight while the current one is consumed.
+//   * Vector-ALU work per score is one FMA, one exp2 and one add, plus a
+//     share of max3 and bf16 packing; two waves per SIMD overlap one wave's
+//     exponentials with the other's MFMAs.
+//   * The reference max used in the exponent is only moved when a row max
+//     grows by more than 2^8 (in the exp2 domain); until then the
+//     accumulator is not rescaled. The result is unchanged because O and l
+//     share the reference; fp32 holds the at most 256x larger terms.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
 namespace fa {
 
-// 16-byte chunk swizzles of a [rows][D] bf16 tile in LDS.
-// K is read row-wise by 32 consecutive rows at one chunk: XOR with the row.
-template <int D>
-__device__ __forceinline__ uint32_t k_off(int row, int chunk) {
-  constexpr int CH = D / 8;
-  return (uint32_t)(row * D * 2 + ((chunk ^ (row & (CH - 1))) << 4));
-}
-// V is read with the transposing read: 8 rows x 64 bytes per wave. XOR the
-// chunk with 4*row so that neighbouring rows land in different 64-byte
-// bank groups.
-template <int D>
-__device__ __forceinline__ uint32_t v_off(int row, int col) {
-  constexpr int CH = D / 8;
-  return (uint32_t)(row * D * 2 + ((((col >> 3) ^ ((row * 4) & (CH - 1)))) << 4) + ((col & 7) << 1));
-}
+// Copying a ROWS x D bf16 tile into a swizzled LDS tile (see tile_off) with
+// the four waves of the workgroup: wave w issues NI 1-KiB copies; lane l of
+// copy i fills 16 bytes of row `row`, physical chunk l % CH, which holds
+// logical chunk (l % CH) ^ swizzle(row).
+template <int D, int ROWS>
+struct TileCopy {
+  static constexpr int CH = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;  // rows per wave-wide copy
+  static constexpr int NI = ROWS / RPI / 4;
+  static_assert(NI * RPI * 4 == ROWS, "tile rows must split over 4 waves");
+  int off[NI];  // element offset of this lane's chunk from the tile's first row
+
+  __device__ __forceinline__ static int row_of(int w, int i, int lane) { return (w * NI + i) * RPI + lane / CH; }
+  __device__ __forceinline__ static int chunk_of(int row, int lane) {
+    constexpr int G = CH / 4;
+    const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
+    return (lane % CH) ^ sw;
+  }
+  __device__ __forceinline__ TileCopy(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_of(w, i, lane);
+      off[i] = row * D + 8 * chunk_of(row, lane);
+    }
+  }
+  // Full tile: rows [0, ROWS) of the matrix starting at g are all valid.
+  __device__ __forceinline__ void full(const uint16_t* g, FA_LDS uint8_t* lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(g + off[i], lds + (w * NI + i) * 1024);
+  }
+  // Tail tile: rows at or past rows_valid repeat the last valid row (the
+  // caller masks them).
+  __device__ __forceinline__ void tail(const uint16_t* g, int rows_valid, FA_LDS uint8_t* lds, int w, int lane) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_of(w, i, lane);
+      const int grow = min(row, rows_valid - 1);
+      dma16(g + grow * D + 8 * chunk_of(row, lane), lds + (w * NI + i) * 1024);
+    }
+  }
+};
 
 template <int D, int BN, bool CAUSAL, bool SPARSE, bool DEBUG>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = FWD_BM;
-  constexpr int CH = D / 8;
   constexpr int TILEB = BN * D * 2;
-  constexpr int LOADS = BN * CH / 256;
-  static_assert(LOADS * 256 == BN * CH, "tile must split evenly over 256 threads");
+  constexpr int NS = BN / 32;  // 32-key blocks per tile
+  constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 domain)
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILEB];
-  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+  // Two LDS stages for K and two for V, as four separate objects: the stage
+  // of every access is a compile-time constant (the loop is unrolled by
+  // two), so the compiler can tell the in-flight copies from the reads and
+  // does not insert waits for the copies before reading the other stage.
+  __shared__ __attribute__((aligned(1024))) uint8_t k0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1_raw[TILEB];
+  FA_LDS uint8_t* const kst[2] = {(FA_LDS uint8_t*)k0_raw, (FA_LDS uint8_t*)k1_raw};
+  FA_LDS uint8_t* const vst[2] = {(FA_LDS uint8_t*)v0_raw, (FA_LDS uint8_t*)v1_raw};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
@@ -68,8 +110,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
 
   const int q_lo = qt * BM;
   const int q_last = min(q_lo + BM, N) - 1;
-  const int q0 = q_lo + 32 * w;          // first query of this wave
-  const int qi = q0 + (lane & 31);       // query of this lane
+  const int q0 = q_lo + 32 * w;     // first query of this wave
+  const int qi = q0 + (lane & 31);  // query of this lane
   int kt_end = p.n_kt;
   if (CAUSAL) kt_end = min(kt_end, q_last / BN + 1);
   const uint8_t* mrow = SPARSE ? p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb : nullptr;
@@ -78,150 +120,135 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
       while (j < kt_end && mrow[(j * BN) / MASK_BLOCK] == 0) ++j;
     return j;
   };
+  // Whether any query of this wave sees any key of tile j.
+  auto wave_active = [&](int j) { return !CAUSAL || j * BN <= q0 + 31; };
 
   // Q^T fragment (B operand): lane holds Q[qi][16*kk + 8*h2 .. +7].
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qrow = p.q + head + (size_t)qi * D + 8 * h2;
+    const uint16_t* qrow = p.q + head + (size_t)min(qi, N - 1) * D + 8 * h2;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (qi < N) t = ld_global16(qrow + 16 * kk);
-      qf[kk] = __builtin_bit_cast(bf16x8, t);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(qrow + 16 * kk));
   }
 
   const uint16_t* kg = p.k + head;
   const uint16_t* vg = p.v + head;
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      const int key = j * BN + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        a = ld_global16(kg + (size_t)key * D + 8 * c);
-        b = ld_global16(vg + (size_t)key * D + 8 * c);
-      }
-      kreg[u] = a;
-      vreg[u] = b;
-    }
-  };
-  auto swrite = [&](int stage) {
-    FA_LDS uint8_t* ks = smem + stage * 2 * TILEB;
-    FA_LDS uint8_t* vs = ks + TILEB;
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      st_lds16(ks, k_off<D>(row, c), kreg[u]);
-      st_lds16(vs, v_off<D>(row, 8 * c), vreg[u]);
+  const TileCopy<D, BN> cp(w, lane);
+  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) {
+    const size_t o = (size_t)j * BN * D;
+    if (j * BN + BN <= N) {
+      cp.full(kg + o, kdst, w);
+      cp.full(vg + o, vdst, w);
+    } else {
+      cp.tail(kg + o, N - j * BN, kdst, w, lane);
+      cp.tail(vg + o, N - j * BN, vdst, w, lane);
     }
   };
 
-  float m_run = -INFINITY;  // running max of S * c (log2 domain)
-  float l_run = 0.f;        // running sum of exp2(S*c - m_run), this lane's keys
+  // S^T tile = K_j Q^T from an LDS stage.
+  auto scores = [&](const FA_LDS uint8_t* ks, f32x16 (&s)[NS]) {
+#pragma unroll
+    for (int mt = 0; mt < NS; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+    // k-step outer so consecutive MFMAs go to independent accumulators
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < NS; ++mt)
+        s[mt] = mfma32(ld_lds16(ks, tile_off<D>(32 * mt + (lane & 31), 16 * kk + 8 * h2)), qf[kk], s[mt]);
+  };
+
+  float m_run = -INFINITY;  // reference max of S * c (log2 domain)
+  float l_run = 0.f;        // sum of exp2(S*c - m_run) over this lane's keys
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-
   const float c = p.c;
-  int j = next_tile(0);
-  if (j < kt_end) {
-    gload(j);
-    swrite(0);
-  }
-  __syncthreads();
-  int stage = 0;
-  while (j < kt_end) {
-    const int jn = next_tile(j + 1);
-    if (jn < kt_end) gload(jn);
-    const int kbase = j * BN;
-    if (DEBUG && tid == 0) p.visited[((size_t)bh * p.n_qt + qt) * p.n_kt + j] = 1;
-    // A wave whose 32 queries all precede the tile's first key skips it.
-    const bool wave_active = !CAUSAL || kbase <= q0 + 31;
-    if (wave_active) {
-      const FA_LDS uint8_t* ks = smem + stage * 2 * TILEB;
-      const FA_LDS uint8_t* vs = ks + TILEB;
-      f32x16 s[BN / 32];
+  const int g = lane >> 4, jj = lane & 15;
+  const int vrow = 4 * h2 + (jj >> 2);
+  const int vcol = 16 * (g & 1) + 4 * (jj & 3);
+
+  // Online softmax of one score tile and O^T += V^T P^T.
+  auto softmax_pv = [&](f32x16 (&s)[NS], int j, const FA_LDS uint8_t* vs, bool need_mask) {
+    if (need_mask) {
+      // Value r of block mt is key j*BN + 32*mt + 8*(r/4) + 4*h2 + r%4; it is
+      // visible iff key <= min(N - 1, qi) (causal) or key <= N - 1.
+      const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - j * BN - 4 * h2;
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt) {
+      for (int mt = 0; mt < NS; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-        const int row = 32 * mt + (lane & 31);
+        for (int r = 0; r < 16; ++r)
+          if (32 * mt + 8 * (r >> 2) + (r & 3) > lim) s[mt][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s[mt] = mfma32(ld_lds16(ks, k_off<D>(row, 2 * kk + h2)), qf[kk], s[mt]);
-      }
-      // Mask only tiles that straddle the diagonal or the end of the sequence.
-      const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0);
-      if (need_mask) {
+    for (int mt = 0; mt < NS; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < BN / 32; ++mt)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+    mx = xhalf_max(mx) * c;
+    const bool grow = mx > m_run + TAU;
+    const float m_new = grow ? mx : m_run;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+      l_run *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 32 * mt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) s[mt][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt)
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    m_run = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    // P^T as B operand: slot i of half h2 in k-step kk is key
+    // 16*kk + 8*(i/4) + 4*h2 + i%4, i.e. value r = 8*(kk%2) + i of block kk/2.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.f;
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      const f32x16& t = s[kk >> 1];
+      const int r0 = 8 * (kk & 1);
+      float e[8];
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[mt][r], c, -m_use));
-          s[mt][r] = e;
-          lsum += e;
-        }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-      // P^T as B operand: slot i of half h2 in k-step kk is key
-      // 16*kk + 8*(i/4) + 4*h2 + i%4, i.e. value r = 8*(kk%2) + i of tile kk/2.
-      bf16x8 pb[BN / 16];
-#pragma unroll
-      for (int kk = 0; kk < BN / 16; ++kk) {
-        const f32x16& t = s[kk >> 1];
-        const int r0 = 8 * (kk & 1);
-        pb[kk] = to_bf16x8(t[r0], t[r0 + 1], t[r0 + 2], t[r0 + 3], t[r0 + 4], t[r0 + 5], t[r0 + 6], t[r0 + 7]);
-      }
-      // V^T as A operand via transposing reads: the lane group of 16 picks
-      // rows 16*kk + 4*h2 (+8) and columns 32*dt + 16*((lane/16)&1).
-      const int g = lane >> 4, jj = lane & 15;
-      const int vrow = 4 * h2 + (jj >> 2);
-      const int vcol = 16 * (g & 1) + 4 * (jj & 3);
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(t[r0 + i], c, -m_use));
+      l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int kk = 0; kk < BN / 16; ++kk) {
-          const s16x4 lo = ld_lds_tr(vs, v_off<D>(16 * kk + vrow, 32 * dt + vcol));
-          const s16x4 hi = ld_lds_tr(vs, v_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol));
-          oacc[dt] = mfma32(join_tr(lo, hi), pb[kk], oacc[dt]);
-        }
+        const s16x4 lo = ld_lds_tr(vs, tile_off<D>(16 * kk + vrow, 32 * dt + vcol));
+        const s16x4 hi = ld_lds_tr(vs, tile_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol));
+        oacc[dt] = mfma32(join_tr(lo, hi), pb, oacc[dt]);
       }
+      // Keep the scheduler from hoisting every V read of the tile at once
+      // (that would exceed the 256-register budget of two waves per SIMD).
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (jn < kt_end) swrite(stage ^ 1);
+  };
+
+  int jc = next_tile(0);
+  if (jc < kt_end) {
+    dma_kv(jc, kst[0], vst[0]);
+    wait_vmem();
     __syncthreads();
-    stage ^= 1;
-    j = jn;
+    // One step (parity P = index of the current tile mod 2): tile jc is in
+    // stage P; the next visited tile is copied into stage 1-P meanwhile.
+    auto step = [&](auto parity) -> bool {
+      constexpr int P = decltype(parity)::value;
+      const int jn = next_tile(jc + 1);
+      if (jn < kt_end) dma_kv(jn, kst[1 - P], vst[1 - P]);
+      if (DEBUG && tid == 0) p.visited[((size_t)bh * p.n_qt + qt) * p.n_kt + jc] = 1;
+      if (wave_active(jc)) {
+        f32x16 s[NS];
+        scores(kst[P], s);
+        const bool need_mask = (jc * BN + BN > N) || (CAUSAL && jc * BN + BN - 1 > q0);
+        softmax_pv(s, jc, vst[P], need_mask);
+      }
+      wait_vmem();
+      __syncthreads();
+      jc = jn;
+      return jn < kt_end;
+    };
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    }
   }
 
   // Epilogue: O = acc / l (deferred normalisation), lse = ln sum exp.
