@@ -32,10 +32,14 @@ int check_common(int B, int H, int N, int d, float scale) {
   return FA_OK;
 }
 
-size_t workspace_bytes_for(int B, int H, int N) {
-  const size_t rows = (size_t)B * H * N;
+int padded_rows(int N) { return (N + fa::BWD_PAD_ROWS - 1) / fa::BWD_PAD_ROWS * fa::BWD_PAD_ROWS; }
+
+// Two fp32 arrays of B*H*Npad rows: D = rowsum(dO * O) and lse * log2(e).
+size_t workspace_half(int B, int H, int N) {
+  const size_t rows = (size_t)B * H * padded_rows(N);
   return (rows * sizeof(float) + 255) & ~(size_t)255;
 }
+size_t workspace_bytes_for(int B, int H, int N) { return 2 * workspace_half(B, H, N); }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
              int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream) {
@@ -86,11 +90,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.Dvec = static_cast<float*>(workspace);
+  p.lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + workspace_half(B, H, N));
   p.mask = mask;
   p.visited_kv = visited_kv;
   p.visited_q = visited_q;
   p.H = H;
   p.N = N;
+  p.Npad = padded_rows(N);
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
@@ -149,7 +155,7 @@ int fa_tile_config(int pass, int d, int* bm, int* bn) {
   switch (pass) {
     case 0: *bm = fa::FWD_BM; *bn = fa::FWD_BN; return FA_OK;
     case 1: *bm = fa::BWD_KV_BM; *bn = fa::BWD_KV_BN; return FA_OK;
-    case 2: *bm = fa::BWD_Q_BM; *bn = fa::BWD_Q_BN; return FA_OK;
+    case 2: *bm = fa::BWD_Q_BM; *bn = d == 128 ? fa::bwd_q_bn<128>() : fa::bwd_q_bn<64>(); return FA_OK;
     default: return FA_ERR_SHAPE;
   }
 }

@@ -8,30 +8,50 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_k dO_ik O_ik,
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 // Three kernels, enqueued in order on one stream:
-//   1. fa_bwd_pre_kernel   D = rowsum(dO o O) into the workspace;
+//   1. fa_bwd_pre_kernel   per row: D = rowsum(dO o O) and lse * log2(e)
+//                          into the workspace, whose rows are padded per head
+//                          to a multiple of 128 (padding: D = 0, lse = +inf,
+//                          so a padded or fully masked row has P = 0 without
+//                          any test in the hot loops);
 //   2. fa_bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile),
 //                          streaming 64-row query tiles; dK, dV stay in
 //                          registers for the whole sweep;
 //   3. fa_bwd_dq_kernel    one workgroup per (batch, head, 128-query tile),
 //                          streaming 64-row key tiles (recomputes S and dP).
-// No atomics: every output element is written once, so results are
-// deterministic.
+// dQ is not accumulated with atomics: fp32 global atomics run at a fraction
+// of the plain store rate on this GPU, and the separate pass keeps every
+// output written once, so results are deterministic.
+//
+// Both attention kernels copy their streamed tiles HBM -> LDS with
+// global_load_lds (no register staging) into two LDS stages whose index is
+// a compile-time constant (the tile loop is unrolled by two), so the next
+// tile's copy is in flight while the current one is consumed, with one
+// barrier per tile. Two workgroups (eight waves) share a CU, so one wave's
+// exponentials overlap another's matrix products.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
 namespace fa {
 
-// ------------------------------------------------------------------ D = rowsum(dO o O)
+// ------------------------------------------------------------------ D = rowsum(dO o O), lse * log2(e)
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dO,
-                                                         float* __restrict__ Dvec, size_t rows) {
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ Dvec, float* __restrict__ lse2,
+                                                         int N, int Npad, size_t rows_pad) {
   constexpr int CH = D / 8;      // lanes per row, 8 elements each
   constexpr int RPB = 256 / CH;  // rows per workgroup
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / CH;
+  const size_t prow = (size_t)blockIdx.x * RPB + threadIdx.x / CH;
   const int c = threadIdx.x % CH;
+  const size_t bh = prow / Npad;
+  const int r = (int)(prow - bh * Npad);
+  const bool real = prow < rows_pad && r < N;
+  const size_t row = bh * N + r;
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const u32x4 a = ld_global16(o + row * D + 8 * c);
     const u32x4 b = ld_global16(dO + row * D + 8 * c);
 #pragma unroll
@@ -42,25 +62,53 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) Dvec[row] = acc;
+  if (prow < rows_pad && c == 0) {
+    float l2 = INFINITY;
+    if (real) {
+      const float l = lse[row];
+      l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+    Dvec[prow] = acc;
+    lse2[prow] = l2;
+  }
 }
 
 // ------------------------------------------------------------------ dK, dV
+// A workgroup of 8 waves owns 128 keys. Waves w and w + 4 share keys
+// 32w .. 32w + 31 and split the four products of every query block evenly:
+//   P-wave  (w < 4):  holds K; S = Q K^T, P = exp2(S*c - lse*log2e), passes
+//                     P (bf16) to its partner through LDS; dV^T += dO^T P.
+//   dS-wave (w >= 4): holds V; dP = dO V^T, reads P, dS = P o (dP - D);
+//                     dK^T += Q^T dS.
+// Each wave keeps one operand (32 keys x d) and one accumulator in
+// registers, so a SIMD runs one wave of each role and overlaps one's
+// vector work with the other's matrix products.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int BNK = BWD_KV_BN;  // keys per workgroup (32 per wave)
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int BNK = BWD_KV_BN;  // keys per workgroup
   constexpr int BMQ = BWD_KV_BM;  // query rows per streamed tile
-  constexpr int CH = D / 8;
+  constexpr int QB = BMQ / 32;    // 32-query blocks per tile
   constexpr int TILEB = BMQ * D * 2;
-  constexpr int LOADS = BMQ * CH / 256;
-  constexpr int STAGEB = 2 * TILEB + 2 * BMQ * 4;  // Q, dO, lse*log2e, D
-  static_assert(LOADS * 256 == BMQ * CH, "tile must split evenly over 256 threads");
   static_assert(BNK == MASK_BLOCK, "one key tile per mask column");
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * STAGEB];
-  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+  static_assert(BMQ == 64, "lse/D rows are copied by one wave-wide 4-byte copy");
+  __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t o0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t o1_raw[TILEB];
+  __shared__ __attribute__((aligned(256))) float l0_raw[2 * BMQ];  // lse*log2e, then D
+  __shared__ __attribute__((aligned(256))) float l1_raw[2 * BMQ];
+  // P of every (key group, query block), in the MFMA result layout: lane l
+  // of key group kg stores its 16 values (32 bytes) at [kg][qb][l].
+  __shared__ __attribute__((aligned(1024))) uint8_t px_raw[4 * QB * 64 * 32];
+  FA_LDS uint8_t* const qst[2] = {(FA_LDS uint8_t*)q0_raw, (FA_LDS uint8_t*)q1_raw};
+  FA_LDS uint8_t* const ost[2] = {(FA_LDS uint8_t*)o0_raw, (FA_LDS uint8_t*)o1_raw};
+  FA_LDS float* const lst[2] = {(FA_LDS float*)l0_raw, (FA_LDS float*)l1_raw};
+  FA_LDS uint8_t* const px = (FA_LDS uint8_t*)px_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
+  const bool dswave = w >= 4;  // wave-uniform role
+  const int kg = w & 3;        // key group shared by waves kg and kg + 4
   const int n_kt = (p.N + BNK - 1) / BNK;
   const int n_qt = (p.N + BMQ - 1) / BMQ;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
@@ -70,37 +118,27 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
   const int kb = jt * BNK;
-  const int k0w = kb + 32 * w;           // first key of this wave
-  const int key = k0w + (lane & 31);     // key of this lane
+  const int k0w = kb + 32 * kg;       // first key of this wave
+  const int key = k0w + (lane & 31);  // key of this lane
 
-  // K and V rows of this lane's key as B operands (d slots 16*kk + 8*h2 + i).
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K (P-wave) or V (dS-wave) rows of this lane's key as B operands
+  // (d slots 16*kk + 8*h2 + i). Keys past N load a copy of key N-1; their
+  // gradients are never stored.
+  bf16x8 kvf[D / 16];
   {
-    const uint16_t* kr = p.k + head + (size_t)key * D + 8 * h2;
-    const uint16_t* vr = p.v + head + (size_t)key * D + 8 * h2;
+    const uint16_t* src = (dswave ? p.v : p.k) + head + (size_t)min(key, N - 1) * D + 8 * h2;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        a = ld_global16(kr + 16 * kk);
-        b = ld_global16(vr + 16 * kk);
-      }
-      kf[kk] = __builtin_bit_cast(bf16x8, a);
-      vf[kk] = __builtin_bit_cast(bf16x8, b);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) kvf[kk] = __builtin_bit_cast(bf16x8, ld_global16(src + 16 * kk));
   }
-  f32x16 dkt[D / 32], dvt[D / 32];
+  f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave)
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkt[dt][r] = 0.f;
-      dvt[dt][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   const int it_begin = CAUSAL ? kb / BMQ : 0;
   const uint8_t* mcol = SPARSE ? p.mask + (size_t)h * p.nb * p.nb + jt : nullptr;
-  auto next_tile = [&](int i) {
+  auto next_tile = [&](int i) __attribute__((always_inline)) {
     if (SPARSE)
       while (i < n_qt && mcol[(size_t)((i * BMQ) / MASK_BLOCK) * p.nb] == 0) ++i;
     return i;
@@ -108,160 +146,171 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 
   const uint16_t* qg = p.q + head;
   const uint16_t* dog = p.dO + head;
-  const float* lseg = p.lse + (size_t)bh * N;
-  const float* Dg = p.Dvec + (size_t)bh * N;
-  u32x4 qreg[LOADS], doreg[LOADS];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int i) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      const int q = i * BMQ + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (q < N) {
-        a = ld_global16(qg + (size_t)q * D + 8 * c);
-        b = ld_global16(dog + (size_t)q * D + 8 * c);
-      }
-      qreg[u] = a;
-      doreg[u] = b;
+  const float* l2g = p.lse2 + (size_t)bh * p.Npad;
+  const float* Dg = p.Dvec + (size_t)bh * p.Npad;
+  const TileCopy<D, BMQ, 8> cp(w, lane);
+  // Query tile i -> LDS: Q and dO rows (rows past N repeat row N-1; their
+  // lse is +inf in the padded workspace, so they contribute P = 0), and the
+  // 64 lse*log2e and D values (waves 0 and 1, 4 bytes per lane).
+  auto dma_q = [&](int i, FA_LDS uint8_t* qdst, FA_LDS uint8_t* odst, FA_LDS float* ldst)
+                   __attribute__((always_inline)) {
+    const size_t o = (size_t)i * BMQ * D;
+    if (i * BMQ + BMQ <= N) {
+      cp.full(qg + o, qdst, w);
+      cp.full(dog + o, odst, w);
+    } else {
+      cp.tail(qg + o, N - i * BMQ, qdst, w, lane);
+      cp.tail(dog + o, N - i * BMQ, odst, w, lane);
     }
-    if (tid < BMQ) {
-      const int q = i * BMQ + tid;
-      // Rows past N or with no visible key get +inf so that P = exp2(. - inf) = 0.
-      float l2 = INFINITY, dd = 0.f;
-      if (q < N) {
-        const float l = lseg[q];
-        l2 = l == -INFINITY ? INFINITY : l * kLog2e;
-        dd = Dg[q];
-      }
-      lreg = l2;
-      dreg = dd;
-    }
-  };
-  auto swrite = [&](int stage) {
-    FA_LDS uint8_t* qs = smem + stage * STAGEB;
-    FA_LDS uint8_t* dos = qs + TILEB;
-    FA_LDS float* ls = (FA_LDS float*)(dos + TILEB);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      st_lds16(qs, tile_off<D>(row, 8 * c), qreg[u]);
-      st_lds16(dos, tile_off<D>(row, 8 * c), doreg[u]);
-    }
-    if (tid < BMQ) {
-      ls[tid] = lreg;
-      ls[BMQ + tid] = dreg;
-    }
+    if (w == 0) __builtin_amdgcn_global_load_lds(l2g + i * BMQ + lane, ldst, 4, 0, 0);
+    if (w == 1) __builtin_amdgcn_global_load_lds(Dg + i * BMQ + lane, ldst + BMQ, 4, 0, 0);
   };
 
   const float c = p.c;
-  int i = next_tile(it_begin);
-  if (i < n_qt) {
-    gload(i);
-    swrite(0);
-  }
-  __syncthreads();
-  int stage = 0;
-  const int g = lane >> 4, jj = lane & 15;
-  const int trow = 4 * h2 + (jj >> 2);
-  const int tcol = 16 * (g & 1) + 4 * (jj & 3);
-  while (i < n_qt) {
-    const int in = next_tile(i + 1);
-    if (in < n_qt) gload(in);
-    if (DEBUG && tid == 0) p.visited_kv[((size_t)bh * n_kt + jt) * n_qt + i] = 1;
-    const FA_LDS uint8_t* qs = smem + stage * STAGEB;
-    const FA_LDS uint8_t* dos = qs + TILEB;
-    const FA_LDS float* ls = (const FA_LDS float*)(dos + TILEB);
+
+  // Phase 1 of a tile: S (P-wave) or dP (dS-wave) for each query block; the
+  // P-wave turns S into bf16 P, keeps it and writes it for its partner.
+  // Phase 2 (after a barrier): dV^T += dO^T P or dK^T += Q^T dS.
+  auto tile = [&](int i, const FA_LDS uint8_t* qs, const FA_LDS uint8_t* dos, const FA_LDS float* ls,
+                  auto last) __attribute__((always_inline)) {
+    // Lane-derived offsets are recomputed here so that they are not hoisted
+    // out of the loop for both unrolled copies at once.
+    int ln = tid & 63;
+    asm volatile("" : "+v"(ln));
+    const int hh = ln >> 5, g = ln >> 4, jj = ln & 15;
+    const int trow = 4 * hh + (jj >> 2);
+    const int tcol = 16 * (g & 1) + 4 * (jj & 3);
+    const int arow = ln & 31;
+    const FA_LDS uint8_t* a1 = dswave ? dos : qs;  // phase-1 A operand rows
+    const FA_LDS uint8_t* a2 = dswave ? qs : dos;  // phase-2 A operand (transposed)
+    f32x16 sd[QB];  // S or dP per query block
+    bf16x8 pb[QB][2];
+    bool live[QB];
 #pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const int qbase = i * BMQ + 32 * qb;
-      if (CAUSAL && qbase + 31 < k0w) continue;  // every query of the block precedes every key of the wave
-      f32x16 s, dp;
+      live[qb] = !(CAUSAL && qbase + 31 < k0w);  // false: every query precedes every key
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+      for (int r = 0; r < 16; ++r) sd[qb][r] = 0.f;
+      if (live[qb]) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          sd[qb] = mfma32(ld_lds16(a1, tile_off<D>(32 * qb + arow, 16 * kk + 8 * hh)), kvf[kk], sd[qb]);
       }
-      const int arow = 32 * qb + (lane & 31);
+    }
+    if (!dswave) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32(ld_lds16(qs, tile_off<D>(arow, 16 * kk + 8 * h2)), kf[kk], s);
-        dp = mfma32(ld_lds16(dos, tile_off<D>(arow, 16 * kk + 8 * h2)), vf[kk], dp);
-      }
-      // value r of this lane is query qbase + 8*(r/4) + 4*h2 + r%4, key `key`
-      const bool need_mask = CAUSAL && (k0w + 31 > qbase);
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!live[qb]) continue;
+        const int qbase = i * BMQ + 32 * qb;
+        const bool need_mask = CAUSAL && (k0w + 31 > qbase);
+        // value r of this lane is query qbase + 8*(r/4) + 4*hh + r%4, key `key`
+        float pe[16];
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int ql = 32 * qb + 8 * rg + 4 * h2;
-        const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + ql);
-        const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + BMQ + ql);
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 32 * qb + 8 * rg + 4 * hh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rg + e;
-          float pe = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (need_mask && key > qbase + 8 * rg + 4 * h2 + e) pe = 0.f;
-          s[r] = pe;
-          dp[r] = pe * (dp[r] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            pe[r] = fast_exp2(fmaf(sd[qb][r], c, -l4[e]));
+            if (need_mask && key > qbase + 8 * rg + 4 * hh + e) pe[r] = 0.f;
+          }
         }
+        pb[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+        pb[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+        FA_LDS uint8_t* dst = px + ((kg * QB + qb) * 64 + ln) * 32;
+        *reinterpret_cast<FA_LDS bf16x8*>(dst) = pb[qb][0];
+        *reinterpret_cast<FA_LDS bf16x8*>(dst + 16) = pb[qb][1];
       }
-      bf16x8 pb[2], dsb[2];
+    }
+    __syncthreads();
+    if (dswave) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!live[qb]) continue;
+        const FA_LDS uint8_t* src = px + ((kg * QB + qb) * 64 + ln) * 32;
+        const bf16x8 p0 = *reinterpret_cast<const FA_LDS bf16x8*>(src);
+        const bf16x8 p1 = *reinterpret_cast<const FA_LDS bf16x8*>(src + 16);
+        float ds[16];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + BMQ + 32 * qb + 8 * rg + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            const float pv = (float)(r < 8 ? p0[r] : p1[r - 8]);
+            ds[r] = pv * (sd[qb][r] - d4[e]);
+          }
+        }
+        pb[qb][0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        pb[qb][1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+      }
+    }
+    // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave); query slots of
+    // k-step ks are 16*ks + 8*(i/4) + 4*hh + i%4 on both operands.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (!live[qb]) continue;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 8 * ks;
-        pb[ks] = to_bf16x8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5], s[r0 + 6], s[r0 + 7]);
-        dsb[ks] = to_bf16x8(dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3], dp[r0 + 4], dp[r0 + 5], dp[r0 + 6], dp[r0 + 7]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS; query slots of k-step ks are
-      // 16*ks + 8*(i/4) + 4*h2 + i%4 on both operands.
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int dt = 0; dt < D / 32; ++dt) {
           const int rr = 32 * qb + 16 * ks + trow;
           const int cc = 32 * dt + tcol;
-          const bf16x8 doT = join_tr(ld_lds_tr(dos, tile_off<D>(rr, cc)), ld_lds_tr(dos, tile_off<D>(rr + 8, cc)));
-          dvt[dt] = mfma32(doT, pb[ks], dvt[dt]);
-          const bf16x8 qT = join_tr(ld_lds_tr(qs, tile_off<D>(rr, cc)), ld_lds_tr(qs, tile_off<D>(rr + 8, cc)));
-          dkt[dt] = mfma32(qT, dsb[ks], dkt[dt]);
+          const bf16x8 aT = join_tr(ld_lds_tr(a2, tile_off<D>(rr, cc)), ld_lds_tr(a2, tile_off<D>(rr + 8, cc)));
+          acc[dt] = mfma32(aT, pb[qb][ks], acc[dt]);
         }
       }
     }
-    if (in < n_qt) swrite(stage ^ 1);
+  };
+
+  int ic = next_tile(it_begin);
+  if (ic < n_qt) {
+    dma_q(ic, qst[0], ost[0], lst[0]);
+    wait_vmem();
     __syncthreads();
-    stage ^= 1;
-    i = in;
+    auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
+      constexpr int P = decltype(parity)::value;
+      const int in = next_tile(ic + 1);
+      if (in < n_qt) dma_q(in, qst[1 - P], ost[1 - P], lst[1 - P]);
+      if (DEBUG && tid == 0) p.visited_kv[((size_t)bh * n_kt + jt) * n_qt + ic] = 1;
+      tile(ic, qst[P], ost[P], lst[P], parity);
+      wait_vmem();
+      __syncthreads();
+      ic = in;
+      return in < n_qt;
+    };
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    }
   }
 
   if (key < N) {
-    uint16_t* dkr = p.dk + head + (size_t)key * D;
-    uint16_t* dvr = p.dv + head + (size_t)key * D;
-    const float sc = p.scale;
+    uint16_t* dst = (dswave ? p.dk : p.dv) + head + (size_t)key * D;
+    const float sc = dswave ? p.scale : 1.0f;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = 32 * dt + 8 * rg + 4 * h2;
-        *reinterpret_cast<u32x2*>(dkr + d0) = pack4_bf16(dkt[dt][4 * rg] * sc, dkt[dt][4 * rg + 1] * sc,
-                                                         dkt[dt][4 * rg + 2] * sc, dkt[dt][4 * rg + 3] * sc);
-        *reinterpret_cast<u32x2*>(dvr + d0) =
-            pack4_bf16(dvt[dt][4 * rg], dvt[dt][4 * rg + 1], dvt[dt][4 * rg + 2], dvt[dt][4 * rg + 3]);
+        *reinterpret_cast<u32x2*>(dst + d0) = pack4_bf16(acc[dt][4 * rg] * sc, acc[dt][4 * rg + 1] * sc,
+                                                         acc[dt][4 * rg + 2] * sc, acc[dt][4 * rg + 3] * sc);
       }
   }
 }
 
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = BWD_Q_BM;
-  constexpr int BN = BWD_Q_BN;
-  constexpr int CH = D / 8;
+  constexpr int BN = bwd_q_bn<D>();
+  constexpr int NS = BN / 32;
   constexpr int TILEB = BN * D * 2;
-  constexpr int LOADS = BN * CH / 256;
-  static_assert(LOADS * 256 == BN * CH, "tile must split evenly over 256 threads");
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * 2 * TILEB];
-  FA_LDS uint8_t* smem = (FA_LDS uint8_t*)smem_raw;
+  __shared__ __attribute__((aligned(1024))) uint8_t k0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0_raw[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1_raw[TILEB];
+  FA_LDS uint8_t* const kst[2] = {(FA_LDS uint8_t*)k0_raw, (FA_LDS uint8_t*)k1_raw};
+  FA_LDS uint8_t* const vst[2] = {(FA_LDS uint8_t*)v0_raw, (FA_LDS uint8_t*)v1_raw};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
@@ -270,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int bh = lid / n_qt;
   int qt = lid % n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // longest query tiles first
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -281,33 +330,26 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(kt_end, q_last / BN + 1);
   const uint8_t* mrow = SPARSE ? p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb : nullptr;
-  auto next_tile = [&](int j) {
+  auto next_tile = [&](int j) __attribute__((always_inline)) {
     if (SPARSE)
       while (j < kt_end && mrow[(j * BN) / MASK_BLOCK] == 0) ++j;
     return j;
   };
+  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BN <= q0 + 31; };
 
+  // Q^T and dO^T fragments (B operands, lane = query). Queries past N load a
+  // copy of row N-1; their lse is +inf in the padded workspace, so P = 0.
   bf16x8 qf[D / 16], dof[D / 16];
   {
-    const uint16_t* qr = p.q + head + (size_t)qi * D + 8 * h2;
-    const uint16_t* dr = p.dO + head + (size_t)qi * D + 8 * h2;
+    const size_t qr = (size_t)min(qi, N - 1) * D + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (qi < N) {
-        a = ld_global16(qr + 16 * kk);
-        b = ld_global16(dr + 16 * kk);
-      }
-      qf[kk] = __builtin_bit_cast(bf16x8, a);
-      dof[kk] = __builtin_bit_cast(bf16x8, b);
+      qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.q + head + qr + 16 * kk));
+      dof[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.dO + head + qr + 16 * kk));
     }
   }
-  float lse2 = INFINITY, Dq = 0.f;
-  if (qi < N) {
-    const float l = p.lse[(size_t)bh * N + qi];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    Dq = p.Dvec[(size_t)bh * N + qi];
-  }
+  const float lse2 = p.lse2[(size_t)bh * p.Npad + qi];
+  const float Dq = p.Dvec[(size_t)bh * p.Npad + qi];
   f32x16 dqt[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -316,100 +358,96 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
 
   const uint16_t* kg = p.k + head;
   const uint16_t* vg = p.v + head;
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      const int kr = j * BN + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (kr < N) {
-        a = ld_global16(kg + (size_t)kr * D + 8 * c);
-        b = ld_global16(vg + (size_t)kr * D + 8 * c);
-      }
-      kreg[u] = a;
-      vreg[u] = b;
-    }
-  };
-  auto swrite = [&](int stage) {
-    FA_LDS uint8_t* ks = smem + stage * 2 * TILEB;
-    FA_LDS uint8_t* vs = ks + TILEB;
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int idx = u * 256 + tid;
-      const int row = idx / CH, c = idx % CH;
-      st_lds16(ks, tile_off<D>(row, 8 * c), kreg[u]);
-      st_lds16(vs, tile_off<D>(row, 8 * c), vreg[u]);
+  const TileCopy<D, BN> cp(w, lane);
+  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
+    const size_t o = (size_t)j * BN * D;
+    if (j * BN + BN <= N) {
+      cp.full(kg + o, kdst, w);
+      cp.full(vg + o, vdst, w);
+    } else {
+      cp.tail(kg + o, N - j * BN, kdst, w, lane);
+      cp.tail(vg + o, N - j * BN, vdst, w, lane);
     }
   };
 
   const float c = p.c;
-  int j = next_tile(0);
-  if (j < kt_end) {
-    gload(j);
-    swrite(0);
-  }
-  __syncthreads();
-  int stage = 0;
-  const int g = lane >> 4, jj = lane & 15;
-  const int trow = 4 * h2 + (jj >> 2);
-  const int tcol = 16 * (g & 1) + 4 * (jj & 3);
-  while (j < kt_end) {
-    const int jn = next_tile(j + 1);
-    if (jn < kt_end) gload(jn);
+
+  auto tile = [&](int j, const FA_LDS uint8_t* ks, const FA_LDS uint8_t* vs, bool need_mask)
+                  __attribute__((always_inline)) {
+    // Lane-derived offsets are recomputed here so that they are not hoisted
+    // out of the loop for both unrolled copies at once.
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    const int h2 = lane >> 5, g = lane >> 4, jj = lane & 15;
+    const int trow = 4 * h2 + (jj >> 2);
+    const int tcol = 16 * (g & 1) + 4 * (jj & 3);
     const int kbase = j * BN;
-    if (DEBUG && tid == 0) p.visited_q[((size_t)bh * n_qt + qt) * n_kt + j] = 1;
-    const bool wave_active = !CAUSAL || kbase <= q0 + 31;
-    if (wave_active) {
-      const FA_LDS uint8_t* ks = smem + stage * 2 * TILEB;
-      const FA_LDS uint8_t* vs = ks + TILEB;
-      f32x16 s[BN / 32], dp[BN / 32];
+    f32x16 s[NS], dp[NS];
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt) {
+    for (int mt = 0; mt < NS; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[mt][r] = 0.f;
-          dp[mt][r] = 0.f;
-        }
+      for (int r = 0; r < 16; ++r) {
+        s[mt][r] = 0.f;
+        dp[mt][r] = 0.f;
+      }
+    // S^T = K Q^T and dP^T = V dO^T; k-step outer so consecutive products
+    // go to independent accumulators.
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < NS; ++mt) {
         const int row = 32 * mt + (lane & 31);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s[mt] = mfma32(ld_lds16(ks, tile_off<D>(row, 16 * kk + 8 * h2)), qf[kk], s[mt]);
-          dp[mt] = mfma32(ld_lds16(vs, tile_off<D>(row, 16 * kk + 8 * h2)), dof[kk], dp[mt]);
-        }
+        s[mt] = mfma32(ld_lds16(ks, tile_off<D>(row, 16 * kk + 8 * h2)), qf[kk], s[mt]);
+        dp[mt] = mfma32(ld_lds16(vs, tile_off<D>(row, 16 * kk + 8 * h2)), dof[kk], dp[mt]);
       }
-      const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0);
+    // Value r of block mt is key kbase + 32*mt + 8*(r/4) + 4*h2 + r%4; it is
+    // visible iff key <= min(N - 1, qi) (causal) or key <= N - 1.
+    const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - kbase - 4 * h2;
+    // dQ^T += K^T dS^T; key slots of k-step kk are 16*kk + 8*(i/4) + 4*h2 + i%4,
+    // i.e. value r = 8*(kk%2) + i of block kk/2.
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt)
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      const int mt = kk >> 1, r0 = 8 * (kk & 1);
+      bf16x8 dsb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pe = fast_exp2(fmaf(s[mt][r], c, -lse2));
-          if (need_mask) {
-            const int kr = kbase + 32 * mt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (kr >= N || (CAUSAL && kr > qi)) pe = 0.f;
-          }
-          dp[mt][r] = pe * (dp[mt][r] - Dq);
-        }
-      // dQ^T += K^T dS^T; key slots of k-step kk are 16*kk + 8*(i/4) + 4*h2 + i%4.
-#pragma unroll
-      for (int kk = 0; kk < BN / 16; ++kk) {
-        const f32x16& t = dp[kk >> 1];
-        const int r0 = 8 * (kk & 1);
-        const bf16x8 dsb = to_bf16x8(t[r0], t[r0 + 1], t[r0 + 2], t[r0 + 3], t[r0 + 4], t[r0 + 5], t[r0 + 6], t[r0 + 7]);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int rr = 16 * kk + trow;
-          const int cc = 32 * dt + tcol;
-          const bf16x8 kT = join_tr(ld_lds_tr(ks, tile_off<D>(rr, cc)), ld_lds_tr(ks, tile_off<D>(rr + 8, cc)));
-          dqt[dt] = mfma32(kT, dsb, dqt[dt]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        float pe = fast_exp2(fmaf(s[mt][r], c, -lse2));
+        if (need_mask && 32 * mt + 8 * (r >> 2) + (r & 3) > lim) pe = 0.f;
+        dsb[i] = (__bf16)(pe * (dp[mt][r] - Dq));
       }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int rr = 16 * kk + trow;
+        const int cc = 32 * dt + tcol;
+        const bf16x8 kT = join_tr(ld_lds_tr(ks, tile_off<D>(rr, cc)), ld_lds_tr(ks, tile_off<D>(rr + 8, cc)));
+        dqt[dt] = mfma32(kT, dsb, dqt[dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (jn < kt_end) swrite(stage ^ 1);
+  };
+
+  int jc = next_tile(0);
+  if (jc < kt_end) {
+    dma_kv(jc, kst[0], vst[0]);
+    wait_vmem();
     __syncthreads();
-    stage ^= 1;
-    j = jn;
+    auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
+      constexpr int P = decltype(parity)::value;
+      const int jn = next_tile(jc + 1);
+      if (jn < kt_end) dma_kv(jn, kst[1 - P], vst[1 - P]);
+      if (DEBUG && tid == 0) p.visited_q[((size_t)bh * n_qt + qt) * n_kt + jc] = 1;
+      if (wave_active(jc)) {
+        const bool need_mask = (jc * BN + BN > N) || (CAUSAL && jc * BN + BN - 1 > q0);
+        tile(jc, kst[P], vst[P], need_mask);
+      }
+      wait_vmem();
+      __syncthreads();
+      jc = jn;
+      return jn < kt_end;
+    };
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    }
   }
 
   if (qi < N) {
@@ -427,20 +465,20 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------ launchers
-// stages: bit 0 = D preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
+// stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
 hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) {
   if (stages & 1) {
-    const size_t rows = (size_t)BH * p.N;
+    const size_t rows_pad = (size_t)BH * p.Npad;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
-                       p.dO, p.Dvec, rows);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
+                       p.dO, p.lse, p.Dvec, p.lse2, p.N, p.Npad, rows_pad);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
     const int n_kt1 = (p.N + BWD_KV_BN - 1) / BWD_KV_BN;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_kt1)), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_kt1)), dim3(512), 0,
                        st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -120,4 +120,46 @@ __device__ __forceinline__ uint32_t tile_off(int row, int col) {
   return (uint32_t)(row * D * 2 + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1));
 }
 
+// Copying a ROWS x D bf16 tile into a swizzled LDS tile (see tile_off) with
+// the WAVES waves of the workgroup: wave w issues NI 1-KiB copies; lane l of
+// copy i fills 16 bytes of row `row`, physical chunk l % CH, which holds
+// logical chunk (l % CH) ^ swizzle(row).
+template <int D, int ROWS, int WAVES = 4>
+struct TileCopy {
+  static constexpr int CH = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;  // rows per wave-wide copy
+  static constexpr int NI = ROWS / RPI / WAVES;
+  static_assert(NI * RPI * WAVES == ROWS, "tile rows must split over the waves");
+  int off[NI];  // element offset of this lane's chunk from the tile's first row
+
+  __device__ __forceinline__ static int row_of(int w, int i, int lane) { return (w * NI + i) * RPI + lane / CH; }
+  __device__ __forceinline__ static int chunk_of(int row, int lane) {
+    constexpr int G = CH / 4;
+    const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
+    return (lane % CH) ^ sw;
+  }
+  __device__ __forceinline__ TileCopy(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_of(w, i, lane);
+      off[i] = row * D + 8 * chunk_of(row, lane);
+    }
+  }
+  // Full tile: rows [0, ROWS) of the matrix starting at g are all valid.
+  __device__ __forceinline__ void full(const uint16_t* g, FA_LDS uint8_t* lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(g + off[i], lds + (w * NI + i) * 1024);
+  }
+  // Tail tile: rows at or past rows_valid repeat the last valid row (the
+  // caller masks them or gives them zero weight).
+  __device__ __forceinline__ void tail(const uint16_t* g, int rows_valid, FA_LDS uint8_t* lds, int w, int lane) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_of(w, i, lane);
+      const int grow = min(row, rows_valid - 1);
+      dma16(g + grow * D + 8 * chunk_of(row, lane), lds + (w * NI + i) * 1024);
+    }
+  }
+};
+
 }  // namespace fa

@@ -37,48 +37,6 @@
 
 namespace fa {
 
-// Copying a ROWS x D bf16 tile into a swizzled LDS tile (see tile_off) with
-// the four waves of the workgroup: wave w issues NI 1-KiB copies; lane l of
-// copy i fills 16 bytes of row `row`, physical chunk l % CH, which holds
-// logical chunk (l % CH) ^ swizzle(row).
-template <int D, int ROWS>
-struct TileCopy {
-  static constexpr int CH = D / 8;     // 16-byte chunks per row
-  static constexpr int RPI = 64 / CH;  // rows per wave-wide copy
-  static constexpr int NI = ROWS / RPI / 4;
-  static_assert(NI * RPI * 4 == ROWS, "tile rows must split over 4 waves");
-  int off[NI];  // element offset of this lane's chunk from the tile's first row
-
-  __device__ __forceinline__ static int row_of(int w, int i, int lane) { return (w * NI + i) * RPI + lane / CH; }
-  __device__ __forceinline__ static int chunk_of(int row, int lane) {
-    constexpr int G = CH / 4;
-    const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
-    return (lane % CH) ^ sw;
-  }
-  __device__ __forceinline__ TileCopy(int w, int lane) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = row_of(w, i, lane);
-      off[i] = row * D + 8 * chunk_of(row, lane);
-    }
-  }
-  // Full tile: rows [0, ROWS) of the matrix starting at g are all valid.
-  __device__ __forceinline__ void full(const uint16_t* g, FA_LDS uint8_t* lds, int w) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(g + off[i], lds + (w * NI + i) * 1024);
-  }
-  // Tail tile: rows at or past rows_valid repeat the last valid row (the
-  // caller masks them).
-  __device__ __forceinline__ void tail(const uint16_t* g, int rows_valid, FA_LDS uint8_t* lds, int w, int lane) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = row_of(w, i, lane);
-      const int grow = min(row, rows_valid - 1);
-      dma16(g + grow * D + 8 * chunk_of(row, lane), lds + (w * NI + i) * 1024);
-    }
-  }
-};
-
 template <int D, int BN, bool CAUSAL, bool SPARSE, bool DEBUG>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = FWD_BM;
@@ -115,13 +73,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   int kt_end = p.n_kt;
   if (CAUSAL) kt_end = min(kt_end, q_last / BN + 1);
   const uint8_t* mrow = SPARSE ? p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb : nullptr;
-  auto next_tile = [&](int j) {
+  auto next_tile = [&](int j) __attribute__((always_inline)) {
     if (SPARSE)
       while (j < kt_end && mrow[(j * BN) / MASK_BLOCK] == 0) ++j;
     return j;
   };
   // Whether any query of this wave sees any key of tile j.
-  auto wave_active = [&](int j) { return !CAUSAL || j * BN <= q0 + 31; };
+  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BN <= q0 + 31; };
 
   // Q^T fragment (B operand): lane holds Q[qi][16*kk + 8*h2 .. +7].
   bf16x8 qf[D / 16];
@@ -134,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   const uint16_t* kg = p.k + head;
   const uint16_t* vg = p.v + head;
   const TileCopy<D, BN> cp(w, lane);
-  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) {
+  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
     const size_t o = (size_t)j * BN * D;
     if (j * BN + BN <= N) {
       cp.full(kg + o, kdst, w);
@@ -231,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
     __syncthreads();
     // One step (parity P = index of the current tile mod 2): tile jc is in
     // stage P; the next visited tile is copied into stage 1-P meanwhile.
-    auto step = [&](auto parity) -> bool {
+    auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
       constexpr int P = decltype(parity)::value;
       const int jn = next_tile(jc + 1);
       if (jn < kt_end) dma_kv(jn, kst[1 - P], vst[1 - P]);

@@ -10,14 +10,19 @@ namespace fa {
 // the query rows of the tile, never the keys), key/value tiles of FWD_BN rows.
 constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
-// Backward dK/dV kernel: a workgroup owns BWD_KV_BN keys (32 per wave) and
-// streams query tiles of BWD_KV_BM rows.
+// Backward dK/dV kernel: a workgroup of 8 waves owns BWD_KV_BN keys; waves
+// w and w + 4 share keys 32w .. 32w + 31 (one computes P and dV, the other
+// dP, dS and dK). Query tiles of BWD_KV_BM rows stream through LDS.
 constexpr int BWD_KV_BN = 128;
 constexpr int BWD_KV_BM = 64;
 // Backward dQ kernel: a workgroup owns BWD_Q_BM queries (32 per wave) and
-// streams key tiles of BWD_Q_BN rows.
+// streams key tiles of bwd_q_bn<D>() rows (32 at d = 128 keeps a wave within
+// the 256 registers that two waves per SIMD allow).
 constexpr int BWD_Q_BM = 128;
-constexpr int BWD_Q_BN = 64;
+template <int D>
+constexpr int bwd_q_bn() { return D == 128 ? 32 : 64; }
+// Workspace rows per head are padded to a multiple of this.
+constexpr int BWD_PAD_ROWS = 128;
 // Block-sparse masks are given at this granularity.
 constexpr int MASK_BLOCK = 128;
 
@@ -39,16 +44,18 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* o;
-  const float* lse;
   const uint16_t* dO;
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* Dvec;  // workspace: rowsum(dO * O), [B*H*N]
+  const float* lse;  // forward's lse, [B*H*N]
+  float* Dvec;       // workspace: rowsum(dO * O), [B*H][Npad]
+  float* lse2;       // workspace: lse * log2(e) (+inf for no visible key or padding), [B*H][Npad]
   const uint8_t* mask;
   uint8_t* visited_kv;  // [B*H][n_kt1][n_qt1] or nullptr
   uint8_t* visited_q;   // [B*H][n_qt2][n_kt2] or nullptr
   int H, N;
+  int Npad;  // N rounded up to a multiple of BWD_PAD_ROWS
   int nb;
   float c;      // scale * log2(e)
   float scale;  // scale, applied to dQ and dK
