@@ -16,9 +16,10 @@ hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool spars
 
 namespace {
 
-// Largest supported sizes: every row index fits an int with room to spare
-// and B*H*N*d elements fit comfortably in 64-bit offsets.
-constexpr long long kMaxN = 1LL << 24;
+// Largest supported sizes: one head of one tensor (N*d*2 bytes) must be
+// addressable by a 32-bit buffer offset, and B*H*N*d elements fit
+// comfortably in 64-bit offsets.
+constexpr long long kMaxN = 1LL << 22;
 constexpr long long kMaxElems = 1LL << 40;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -144,26 +144,22 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
     return i;
   };
 
-  const uint16_t* qg = p.q + head;
-  const uint16_t* dog = p.dO + head;
+  // Q, dO of this head and its lse*log2e / D rows as buffer resources. Rows
+  // past N read as zero; their lse is +inf in the padded workspace, so they
+  // contribute P = 0.
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const uint32_t row_bytes = (uint32_t)p.Npad * 4;
   const float* l2g = p.lse2 + (size_t)bh * p.Npad;
   const float* Dg = p.Dvec + (size_t)bh * p.Npad;
-  const TileCopy<D, BMQ, 8> cp(w, lane);
-  // Query tile i -> LDS: Q and dO rows (rows past N repeat row N-1; their
-  // lse is +inf in the padded workspace, so they contribute P = 0), and the
-  // 64 lse*log2e and D values (waves 0 and 1, 4 bytes per lane).
+  const TileDMA<D, BMQ, 8> cp(w, lane);
+  // Query tile i -> LDS: Q and dO rows, and the 64 lse*log2e and D values
+  // (waves 0 and 1, 4 bytes per lane).
   auto dma_q = [&](int i, FA_LDS uint8_t* qdst, FA_LDS uint8_t* odst, FA_LDS float* ldst)
                    __attribute__((always_inline)) {
-    const size_t o = (size_t)i * BMQ * D;
-    if (i * BMQ + BMQ <= N) {
-      cp.full(qg + o, qdst, w);
-      cp.full(dog + o, odst, w);
-    } else {
-      cp.tail(qg + o, N - i * BMQ, qdst, w, lane);
-      cp.tail(dog + o, N - i * BMQ, odst, w, lane);
-    }
-    if (w == 0) __builtin_amdgcn_global_load_lds(l2g + i * BMQ + lane, ldst, 4, 0, 0);
-    if (w == 1) __builtin_amdgcn_global_load_lds(Dg + i * BMQ + lane, ldst + BMQ, 4, 0, 0);
+    cp.copy(p.q + head, head_bytes, i * BMQ * D * 2, qdst, w);
+    cp.copy(p.dO + head, head_bytes, i * BMQ * D * 2, odst, w);
+    if (w == 0) dma4(l2g, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)ldst);
+    if (w == 1) dma4(Dg, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)(ldst + BMQ));
   };
 
   const float c = p.c;
@@ -173,10 +169,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   // Phase 2 (after a barrier): dV^T += dO^T P or dK^T += Q^T dS.
   auto tile = [&](int i, const FA_LDS uint8_t* qs, const FA_LDS uint8_t* dos, const FA_LDS float* ls,
                   auto last) __attribute__((always_inline)) {
-    // Lane-derived offsets are recomputed here so that they are not hoisted
-    // out of the loop for both unrolled copies at once.
-    int ln = tid & 63;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane;
     const int hh = ln >> 5, g = ln >> 4, jj = ln & 15;
     const int trow = 4 * hh + (jj >> 2);
     const int tcol = 16 * (g & 1) + 4 * (jj & 3);
@@ -210,11 +203,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
         for (int rg = 0; rg < 4; ++rg) {
           const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 32 * qb + 8 * rg + 4 * hh);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            pe[r] = fast_exp2(fmaf(sd[qb][r], c, -l4[e]));
-            if (need_mask && key > qbase + 8 * rg + 4 * hh + e) pe[r] = 0.f;
-          }
+          for (int e = 0; e < 4; ++e) pe[4 * rg + e] = fast_exp2(fmaf(sd[qb][4 * rg + e], c, -l4[e]));
+        }
+        if (need_mask) {  // only blocks that straddle the diagonal
+          const int lim = key - qbase - 4 * hh;  // masked iff 8*(r/4) + r%4 < lim
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) < lim) pe[r] = 0.f;
         }
         pb[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
         pb[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
@@ -356,29 +351,20 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
 
-  const uint16_t* kg = p.k + head;
-  const uint16_t* vg = p.v + head;
-  const TileCopy<D, BN> cp(w, lane);
+  // K and V of this head as buffer resources: tail rows past N read as zero
+  // (and are masked).
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const TileDMA<D, BN> cp(w, lane);
   auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
-    const size_t o = (size_t)j * BN * D;
-    if (j * BN + BN <= N) {
-      cp.full(kg + o, kdst, w);
-      cp.full(vg + o, vdst, w);
-    } else {
-      cp.tail(kg + o, N - j * BN, kdst, w, lane);
-      cp.tail(vg + o, N - j * BN, vdst, w, lane);
-    }
+    cp.copy(p.k + head, head_bytes, j * BN * D * 2, kdst, w);
+    cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
   };
 
   const float c = p.c;
 
   auto tile = [&](int j, const FA_LDS uint8_t* ks, const FA_LDS uint8_t* vs, bool need_mask)
                   __attribute__((always_inline)) {
-    // Lane-derived offsets are recomputed here so that they are not hoisted
-    // out of the loop for both unrolled copies at once.
-    int lane = tid & 63;
-    asm volatile("" : "+v"(lane));
-    const int h2 = lane >> 5, g = lane >> 4, jj = lane & 15;
+    const int g = lane >> 4, jj = lane & 15;
     const int trow = 4 * h2 + (jj >> 2);
     const int tcol = 16 * (g & 1) + 4 * (jj & 3);
     const int kbase = j * BN;
@@ -408,14 +394,19 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
       const int mt = kk >> 1, r0 = 8 * (kk & 1);
+      float pe[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pe[i] = fast_exp2(fmaf(s[mt][r0 + i], c, -lse2));
+      if (need_mask) {  // diagonal or tail tiles only
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = r0 + i;
+          if (32 * mt + 8 * (r >> 2) + (r & 3) > lim) pe[i] = 0.f;
+        }
+      }
       bf16x8 dsb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        float pe = fast_exp2(fmaf(s[mt][r], c, -lse2));
-        if (need_mask && 32 * mt + 8 * (r >> 2) + (r & 3) > lim) pe = 0.f;
-        dsb[i] = (__bf16)(pe * (dp[mt][r] - Dq));
-      }
+      for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)(pe[i] * (dp[mt][r0 + i] - Dq));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int rr = 16 * kk + trow;

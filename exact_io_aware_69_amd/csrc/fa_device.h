@@ -99,12 +99,8 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane l
-// of the wave writes bytes [16*l, 16*l + 16) after `lds_wave_base`, which must
-// be the same for every lane. Completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const uint16_t* gsrc, FA_LDS uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
-}
+// Wait until this wave's outstanding memory loads (including copies into LDS)
+// have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // Byte offset of element (row, col) of a [rows][D] bf16 tile in LDS whose
@@ -120,45 +116,56 @@ __device__ __forceinline__ uint32_t tile_off(int row, int col) {
   return (uint32_t)(row * D * 2 + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1));
 }
 
+// Buffer resource over `bytes` bytes starting at `base` (raw addressing, no
+// stride). Loads at offsets >= bytes return zero, which is how tail tiles
+// are padded: rows past the end of a head arrive as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Copying a ROWS x D bf16 tile into a swizzled LDS tile (see tile_off) with
-// the WAVES waves of the workgroup: wave w issues NI 1-KiB copies; lane l of
+// the WAVES waves of the workgroup, straight from memory into LDS
+// (buffer_load_dwordx4 ... lds): wave w issues NI 1-KiB copies; lane l of
 // copy i fills 16 bytes of row `row`, physical chunk l % CH, which holds
-// logical chunk (l % CH) ^ swizzle(row).
+// logical chunk (l % CH) ^ swizzle(row). The per-lane byte offsets are
+// computed once; each tile only adds a uniform offset.
+// Copy 4 (dma4) or 16 (dma16) bytes per lane from a buffer of `bytes`
+// bytes at `base`, byte offset lane_off + tile_bytes, into LDS at
+// lds + size * lane. These wrappers are plain (non-template) functions:
+// target builtins reached from template instantiations break the host
+// compilation pass of the kernels.
+__device__ __forceinline__ void dma4(const void* base, uint32_t bytes, int lane_off, int tile_bytes,
+                                     FA_LDS void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 4, lane_off, tile_bytes, 0, 0);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, int lane_off, int tile_bytes,
+                                      FA_LDS void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 16, lane_off, tile_bytes, 0, 0);
+}
+
 template <int D, int ROWS, int WAVES = 4>
-struct TileCopy {
+struct TileDMA {
   static constexpr int CH = D / 8;     // 16-byte chunks per row
   static constexpr int RPI = 64 / CH;  // rows per wave-wide copy
   static constexpr int NI = ROWS / RPI / WAVES;
   static_assert(NI * RPI * WAVES == ROWS, "tile rows must split over the waves");
-  int off[NI];  // element offset of this lane's chunk from the tile's first row
+  int voff[NI];  // byte offset of this lane's chunk from the tile's first row
 
-  __device__ __forceinline__ static int row_of(int w, int i, int lane) { return (w * NI + i) * RPI + lane / CH; }
-  __device__ __forceinline__ static int chunk_of(int row, int lane) {
+  __device__ __forceinline__ TileDMA(int w, int lane) {
     constexpr int G = CH / 4;
-    const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
-    return (lane % CH) ^ sw;
-  }
-  __device__ __forceinline__ TileCopy(int w, int lane) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = row_of(w, i, lane);
-      off[i] = row * D + 8 * chunk_of(row, lane);
+      const int row = (w * NI + i) * RPI + lane / CH;
+      const int sw = ((row % G) * 4 + (row / G) % 4) & (CH - 1);
+      voff[i] = (row * D + 8 * ((lane % CH) ^ sw)) * 2;
     }
   }
-  // Full tile: rows [0, ROWS) of the matrix starting at g are all valid.
-  __device__ __forceinline__ void full(const uint16_t* g, FA_LDS uint8_t* lds, int w) const {
+  // Copy the tile whose first row starts `tile_bytes` into a buffer of
+  // `bytes` bytes at `base` (rows past the end arrive as zeros).
+  __device__ __forceinline__ void copy(const void* base, uint32_t bytes, int tile_bytes, FA_LDS uint8_t* lds,
+                                       int w) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(g + off[i], lds + (w * NI + i) * 1024);
-  }
-  // Tail tile: rows at or past rows_valid repeat the last valid row (the
-  // caller masks them or gives them zero weight).
-  __device__ __forceinline__ void tail(const uint16_t* g, int rows_valid, FA_LDS uint8_t* lds, int w, int lane) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = row_of(w, i, lane);
-      const int grow = min(row, rows_valid - 1);
-      dma16(g + grow * D + 8 * chunk_of(row, lane), lds + (w * NI + i) * 1024);
-    }
+    for (int i = 0; i < NI; ++i) dma16(base, bytes, voff[i], tile_bytes, (FA_LDS void*)(lds + (w * NI + i) * 1024));
   }
 };
 

@@ -89,22 +89,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(qrow + 16 * kk));
   }
 
-  const uint16_t* kg = p.k + head;
-  const uint16_t* vg = p.v + head;
-  const TileCopy<D, BN> cp(w, lane);
+  // K and V of this head as buffer resources: tail rows past N read as zero.
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const TileDMA<D, BN> cp(w, lane);
   auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
-    const size_t o = (size_t)j * BN * D;
-    if (j * BN + BN <= N) {
-      cp.full(kg + o, kdst, w);
-      cp.full(vg + o, vdst, w);
-    } else {
-      cp.tail(kg + o, N - j * BN, kdst, w, lane);
-      cp.tail(vg + o, N - j * BN, vdst, w, lane);
-    }
+    cp.copy(p.k + head, head_bytes, j * BN * D * 2, kdst, w);
+    cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
   };
 
   // S^T tile = K_j Q^T from an LDS stage.
-  auto scores = [&](const FA_LDS uint8_t* ks, f32x16 (&s)[NS]) {
+  auto scores = [&](const FA_LDS uint8_t* ks, f32x16 (&s)[NS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < NS; ++mt)
 #pragma unroll
@@ -130,7 +124,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   const int vcol = 16 * (g & 1) + 4 * (jj & 3);
 
   // Online softmax of one score tile and O^T += V^T P^T.
-  auto softmax_pv = [&](f32x16 (&s)[NS], int j, const FA_LDS uint8_t* vs, bool need_mask) {
+  auto softmax_pv = [&](f32x16 (&s)[NS], int j, const FA_LDS uint8_t* vs, bool need_mask)
+                        __attribute__((always_inline)) {
     if (need_mask) {
       // Value r of block mt is key j*BN + 32*mt + 8*(r/4) + 4*h2 + r%4; it is
       // visible iff key <= min(N - 1, qi) (causal) or key <= N - 1.
