@@ -158,6 +158,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
     // 16*kk + 8*(i/4) + 4*h2 + i%4, i.e. value r = 8*(kk%2) + i of block kk/2.
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
+      // V^T fragments of this k-step first, so the LDS latency is covered
+      // by the exponentials below.
+      bf16x8 vT[D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        vT[dt] = join_tr(ld_lds_tr(vs, tile_off<D>(16 * kk + vrow, 32 * dt + vcol)),
+                         ld_lds_tr(vs, tile_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol)));
       const f32x16& t = s[kk >> 1];
       const int r0 = 8 * (kk & 1);
       float e[8];
@@ -166,13 +173,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
       l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const s16x4 lo = ld_lds_tr(vs, tile_off<D>(16 * kk + vrow, 32 * dt + vcol));
-        const s16x4 hi = ld_lds_tr(vs, tile_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol));
-        oacc[dt] = mfma32(join_tr(lo, hi), pb, oacc[dt]);
-      }
-      // Keep the scheduler from hoisting every V read of the tile at once
-      // (that would exceed the 256-register budget of two waves per SIMD).
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(vT[dt], pb, oacc[dt]);
+      // Order within the k-step: the 8 transposed reads, then the vector
+      // work, then the 4 products; and nothing moves across k-steps (hoisting
+      // every V read of the tile would exceed the register budget of two
+      // waves per SIMD).
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
