@@ -98,7 +98,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   __shared__ __attribute__((aligned(256))) float l0_raw[2 * BMQ];  // lse*log2e, then D
   __shared__ __attribute__((aligned(256))) float l1_raw[2 * BMQ];
   // P of every (key group, query block), in the MFMA result layout: lane l
-  // of key group kg stores its 16 values (32 bytes) at [kg][qb][l].
+  // of key group kg stores its 16 values as two 16-byte halves at
+  // [kg][qb][half][l].
   __shared__ __attribute__((aligned(1024))) uint8_t px_raw[4 * QB * 64 * 32];
   FA_LDS uint8_t* const qst[2] = {(FA_LDS uint8_t*)q0_raw, (FA_LDS uint8_t*)q1_raw};
   FA_LDS uint8_t* const ost[2] = {(FA_LDS uint8_t*)o0_raw, (FA_LDS uint8_t*)o1_raw};
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   FA_LDS uint8_t* const px = (FA_LDS uint8_t*)px_raw;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
+  const int lane = tid & 63, h2 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform (scalar)
   const bool dswave = w >= 4;  // wave-uniform role
   const int kg = w & 3;        // key group shared by waves kg and kg + 4
   const int n_kt = (p.N + BNK - 1) / BNK;
@@ -213,9 +215,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
         }
         pb[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
         pb[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
-        FA_LDS uint8_t* dst = px + ((kg * QB + qb) * 64 + ln) * 32;
+        // Two 1 KiB halves, 16 bytes per lane in each (conflict-free).
+        FA_LDS uint8_t* dst = px + (kg * QB + qb) * 2048 + ln * 16;
         *reinterpret_cast<FA_LDS bf16x8*>(dst) = pb[qb][0];
-        *reinterpret_cast<FA_LDS bf16x8*>(dst + 16) = pb[qb][1];
+        *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) = pb[qb][1];
       }
     }
     __syncthreads();
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (!live[qb]) continue;
-        const FA_LDS uint8_t* src = px + ((kg * QB + qb) * 64 + ln) * 32;
+        const FA_LDS uint8_t* src = px + (kg * QB + qb) * 2048 + ln * 16;
         const bf16x8 p0 = *reinterpret_cast<const FA_LDS bf16x8*>(src);
-        const bf16x8 p1 = *reinterpret_cast<const FA_LDS bf16x8*>(src + 16);
+        const bf16x8 p1 = *reinterpret_cast<const FA_LDS bf16x8*>(src + 1024);
         float ds[16];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
@@ -308,7 +311,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   FA_LDS uint8_t* const vst[2] = {(FA_LDS uint8_t*)v0_raw, (FA_LDS uint8_t*)v1_raw};
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
+  const int lane = tid & 63, h2 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform (scalar)
   const int n_qt = (p.N + BM - 1) / BM;
   const int n_kt = (p.N + BN - 1) / BN;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);

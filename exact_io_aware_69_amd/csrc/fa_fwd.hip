@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   FA_LDS uint8_t* const vst[2] = {(FA_LDS uint8_t*)v0_raw, (FA_LDS uint8_t*)v1_raw};
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h2 = lane >> 5;
+  const int lane = tid & 63, h2 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform (scalar)
 
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int bh = lid / p.n_qt;
