@@ -47,6 +47,8 @@ WORKLOADS = {
     "causal_b8_h16_n2048_d64_fwd": dict(B=8, H=16, N=2048, d=64, causal=True, sparse=False, bwd=False),
     "dense_b8_h16_n2048_d64_fwd": dict(B=8, H=16, N=2048, d=64, causal=False, sparse=False, bwd=False),
     "blocksparse_b2_h16_n8192_d64_fwdbwd": dict(B=2, H=16, N=8192, d=64, causal=False, sparse=True, bwd=True),
+    # dense counterpart of the block-sparse workload (comparison for its skipped work and traffic)
+    "dense_b2_h16_n8192_d64_fwdbwd": dict(B=2, H=16, N=8192, d=64, causal=False, sparse=False, bwd=True),
     "dense_b1_h2_n256_d64_fwd": dict(B=1, H=2, N=256, d=64, causal=False, sparse=False, bwd=False),
 }
 DEFAULT = "causal_b4_h16_n4096_d128_fwdbwd"
@@ -158,6 +160,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-tiles", default=None, metavar="BM,BN",
+                    help="run the forward through fa_fwd_tiles with this tile configuration (tile-size study)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     args = ap.parse_args(argv)
@@ -204,12 +208,16 @@ def main(argv=None):
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
+    tiles = tuple(int(x) for x in args.fwd_tiles.split(",")) if args.fwd_tiles else None
     names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if cfg["bwd"] else [])
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        if mptr is None:
+        if tiles is not None:
+            st = _lib.fa_fwd_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   B, H, N, d, causal, scale, mptr, tiles[0], tiles[1], sptr)
+        elif mptr is None:
             st = _lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                              B, H, N, d, causal, scale, sptr)
         else:
@@ -272,7 +280,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                    "block_sparse": cfg["sparse"], "pass": "fwd+bwd" if cfg["bwd"] else "fwd",
-                   "seed": args.seed, "parallelism": "single GPU"},
+                   "seed": args.seed, "parallelism": "single GPU",
+                   "fwd_tiles": list(tiles) if tiles else [128, 64]},
         "frac_peak": round(value / PEAK_TFLOPS, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_TFLOPS, 4),

@@ -23,6 +23,7 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "fa_fwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]),
+    "fa_fwd_tiles": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_bwd_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
@@ -76,6 +77,10 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
 
 def fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, stream):
     return lib().fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, stream)
+
+
+def fa_fwd_tiles(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, bm, bn, stream):
+    return lib().fa_fwd_tiles(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, bm, bn, stream)
 
 
 def fa_bwd_workspace_size(B, H, N, d):

@@ -9,7 +9,9 @@
 #include "fa_params.h"
 
 namespace fa {
-hipError_t launch_fwd(const FwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st);
+hipError_t launch_fwd(const FwdParams& p, int BH, int d, int bm, int bn, bool causal, bool sparse, bool debug,
+                      hipStream_t st);
+bool fwd_config_supported(int bm, int bn);
 hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
                       hipStream_t st);
 }  // namespace fa
@@ -43,7 +45,8 @@ size_t workspace_half(int B, int H, int N) {
 size_t workspace_bytes_for(int B, int H, int N) { return 2 * workspace_half(B, H, N); }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-             int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream) {
+             int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream,
+             int bm = fa::FWD_BM, int bn = fa::FWD_BN) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale);
   if (st != FA_OK) return st;
@@ -59,11 +62,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.visited = visited;
   p.H = H;
   p.N = N;
-  p.n_qt = (N + fa::FWD_BM - 1) / fa::FWD_BM;
-  p.n_kt = (N + fa::FWD_BN - 1) / fa::FWD_BN;
+  p.n_qt = (N + bm - 1) / bm;
+  p.n_kt = (N + bn - 1) / bn;
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
-  hipError_t e = fa::launch_fwd(p, B * H, d, causal != 0, sparse, visited != nullptr, (hipStream_t)stream);
+  hipError_t e =
+      fa::launch_fwd(p, B * H, d, bm, bn, causal != 0, sparse, visited != nullptr, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -118,6 +122,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                        int causal, float scale, const uint8_t* block_mask, void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, true, nullptr, stream);
+}
+
+int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                 int causal, float scale, const uint8_t* block_mask, int bm, int bn, void* stream) {
+  if (!fa::fwd_config_supported(bm, bn)) return FA_ERR_SHAPE;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, block_mask != nullptr, nullptr, stream,
+                  bm, bn);
 }
 
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {

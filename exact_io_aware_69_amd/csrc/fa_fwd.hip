@@ -37,9 +37,10 @@
 
 namespace fa {
 
-template <int D, int BN, bool CAUSAL, bool SPARSE, bool DEBUG>
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
-  constexpr int BM = FWD_BM;
+template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
+  constexpr int BM = 32 * WAVES;  // query rows per workgroup
+  static_assert(BN <= MASK_BLOCK && BM <= 2 * MASK_BLOCK, "a tile spans at most one mask column, two mask rows");
   constexpr int TILEB = BN * D * 2;
   constexpr int NS = BN / 32;  // 32-key blocks per tile
   constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 domain)
@@ -73,14 +74,27 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   const int qi = q0 + (lane & 31);  // query of this lane
   int kt_end = p.n_kt;
   if (CAUSAL) kt_end = min(kt_end, q_last / BN + 1);
-  const uint8_t* mrow = SPARSE ? p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb : nullptr;
+  // Block-sparse: the query tile spans one or two 128-row mask blocks. The
+  // workgroup visits a key tile when any of them keeps it; a wave computes
+  // it only when the block of its own 32 queries keeps it.
+  const uint8_t* mrow0 = nullptr;
+  const uint8_t* mrow1 = nullptr;
+  const uint8_t* mroww = nullptr;
+  if (SPARSE) {
+    const uint8_t* mh = p.mask + (size_t)h * p.nb * p.nb;
+    mrow0 = mh + (size_t)(q_lo / MASK_BLOCK) * p.nb;
+    mrow1 = mh + (size_t)(q_last / MASK_BLOCK) * p.nb;
+    mroww = mh + (size_t)(min(q0, N - 1) / MASK_BLOCK) * p.nb;
+  }
   auto next_tile = [&](int j) __attribute__((always_inline)) {
     if (SPARSE)
-      while (j < kt_end && mrow[(j * BN) / MASK_BLOCK] == 0) ++j;
+      while (j < kt_end && mrow0[(j * BN) / MASK_BLOCK] == 0 && mrow1[(j * BN) / MASK_BLOCK] == 0) ++j;
     return j;
   };
-  // Whether any query of this wave sees any key of tile j.
-  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BN <= q0 + 31; };
+  // Whether this wave computes tile j: some query of the wave sees some key.
+  auto wave_active = [&](int j) __attribute__((always_inline)) {
+    return (!CAUSAL || j * BN <= q0 + 31) && (!SPARSE || mroww[(j * BN) / MASK_BLOCK] != 0);
+  };
 
   // Q^T fragment (B operand): lane holds Q[qi][16*kk + 8*h2 .. +7].
   bf16x8 qf[D / 16];
@@ -92,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
 
   // K and V of this head as buffer resources: tail rows past N read as zero.
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const TileDMA<D, BN> cp(w, lane);
+  const TileDMA<D, BN, WAVES> cp(w, lane);
   auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
     cp.copy(p.k + head, head_bytes, j * BN * D * 2, kdst, w);
     cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
@@ -231,26 +245,52 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(const FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG>
 hipError_t launch_fwd_t(const FwdParams& p, int BH, hipStream_t st) {
   const dim3 grid((unsigned)(BH * p.n_qt));
-  hipLaunchKernelGGL((fa_fwd_kernel<D, FWD_BN, CAUSAL, SPARSE, DEBUG>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BN, WAVES, CAUSAL, SPARSE, DEBUG>), grid, dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_fwd_d(const FwdParams& p, int BH, bool causal, bool sparse, bool debug, hipStream_t st) {
+template <int D, int BN, int WAVES>
+hipError_t launch_fwd_c(const FwdParams& p, int BH, bool causal, bool sparse, bool debug, hipStream_t st) {
   if (debug) {
-    if (causal) return sparse ? launch_fwd_t<D, true, true, true>(p, BH, st) : launch_fwd_t<D, true, false, true>(p, BH, st);
-    return sparse ? launch_fwd_t<D, false, true, true>(p, BH, st) : launch_fwd_t<D, false, false, true>(p, BH, st);
+    if (causal)
+      return sparse ? launch_fwd_t<D, BN, WAVES, true, true, true>(p, BH, st)
+                    : launch_fwd_t<D, BN, WAVES, true, false, true>(p, BH, st);
+    return sparse ? launch_fwd_t<D, BN, WAVES, false, true, true>(p, BH, st)
+                  : launch_fwd_t<D, BN, WAVES, false, false, true>(p, BH, st);
   }
-  if (causal) return sparse ? launch_fwd_t<D, true, true, false>(p, BH, st) : launch_fwd_t<D, true, false, false>(p, BH, st);
-  return sparse ? launch_fwd_t<D, false, true, false>(p, BH, st) : launch_fwd_t<D, false, false, false>(p, BH, st);
+  if (causal)
+    return sparse ? launch_fwd_t<D, BN, WAVES, true, true, false>(p, BH, st)
+                  : launch_fwd_t<D, BN, WAVES, true, false, false>(p, BH, st);
+  return sparse ? launch_fwd_t<D, BN, WAVES, false, true, false>(p, BH, st)
+                : launch_fwd_t<D, BN, WAVES, false, false, false>(p, BH, st);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, hipStream_t st) {
-  return d == 64 ? launch_fwd_d<64>(p, BH, causal, sparse, debug, st)
-                 : launch_fwd_d<128>(p, BH, causal, sparse, debug, st);
+// Tile configurations compiled in: (query rows per workgroup, keys per
+// tile). The first is the default of fa_fwd; the others exist for the
+// tile-size study (fa_fwd_tiles). Debug visit maps use the default only.
+bool fwd_config_supported(int bm, int bn) {
+  return (bm == 128 && (bn == 32 || bn == 64 || bn == 128)) || (bm == 256 && (bn == 64 || bn == 128));
+}
+
+template <int D>
+hipError_t launch_fwd_d(const FwdParams& p, int BH, int bm, int bn, bool causal, bool sparse, bool debug,
+                        hipStream_t st) {
+  if (debug) return launch_fwd_c<D, FWD_BN, FWD_BM / 32>(p, BH, causal, sparse, true, st);
+  if (bm == 128 && bn == 32) return launch_fwd_c<D, 32, 4>(p, BH, causal, sparse, false, st);
+  if (bm == 128 && bn == 64) return launch_fwd_c<D, 64, 4>(p, BH, causal, sparse, false, st);
+  if (bm == 128 && bn == 128) return launch_fwd_c<D, 128, 4>(p, BH, causal, sparse, false, st);
+  if (bm == 256 && bn == 64) return launch_fwd_c<D, 64, 8>(p, BH, causal, sparse, false, st);
+  if (bm == 256 && bn == 128) return launch_fwd_c<D, 128, 8>(p, BH, causal, sparse, false, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdParams& p, int BH, int d, int bm, int bn, bool causal, bool sparse, bool debug,
+                      hipStream_t st) {
+  return d == 64 ? launch_fwd_d<64>(p, BH, bm, bn, causal, sparse, debug, st)
+                 : launch_fwd_d<128>(p, BH, bm, bn, causal, sparse, debug, st);
 }
 
 }  // namespace fa

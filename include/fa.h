@@ -77,6 +77,19 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, int causal, float scale,
                        const uint8_t* block_mask, void* stream);
 
+/* Forward with an explicit tile configuration, for tile-size studies (the
+ * IO analysis of the Stanford FlashAttention summary: HBM accesses against
+ * on-chip memory size). Same computation and arguments as
+ * fa_fwd_blocksparse (block_mask may be NULL for dense), plus
+ *   bm: query rows per workgroup (128: 4 waves, two workgroups per CU;
+ *       256: 8 waves, one workgroup per CU),
+ *   bn: keys per K/V tile staged in LDS.
+ * Supported (bm, bn): (128, 32), (128, 64), (128, 128), (256, 64),
+ * (256, 128); any other pair returns FA_ERR_SHAPE. fa_fwd uses (128, 64). */
+int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale,
+                 const uint8_t* block_mask, int bm, int bn, void* stream);
+
 /* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need:
  * float32 D = rowsum(dO * O) for every row, O(B*H*N) -- never O(N^2). */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);

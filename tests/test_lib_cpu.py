@@ -154,3 +154,8 @@ def test_expected_visits_blocksparse():
     # key-major map for the dK/dV kernel: [key tile][query tile]
     vk = expected_visits(300, 64, 128, False, mask, key_major=True)[0]
     assert vk.shape == (3, 5) and vk[0].tolist() == [1, 1, 0, 0, 1]
+
+
+def test_fwd_tiles_rejects_unsupported_configs_before_launch():
+    for bm, bn in [(64, 64), (256, 32), (128, 256), (512, 64), (0, 0)]:
+        assert _lib.fa_fwd_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0, 0.125, None, bm, bn, None) == -2
