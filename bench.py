@@ -160,6 +160,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--standard", action="store_true",
+                    help="time the standard attention baseline (materialised S; fa_std_fwd) instead of the "
+                         "IO-aware forward; forward only")
     ap.add_argument("--fwd-tiles", default=None, metavar="BM,BN",
                     help="run the forward through fa_fwd_tiles with this tile configuration (tile-size study)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -187,7 +190,9 @@ def main(argv=None):
         return 0
 
     _lib.lib()  # raises if libfa.so is missing: there is no other path
-    cfg = WORKLOADS[args.workload]
+    cfg = dict(WORKLOADS[args.workload])
+    if args.standard:
+        cfg["bwd"] = False
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     scale = 1.0 / math.sqrt(d)
     inp = make_inputs(args.seed, B, H, N, d, with_do=cfg["bwd"], sparse=cfg["sparse"])
@@ -209,12 +214,20 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     tiles = tuple(int(x) for x in args.fwd_tiles.split(",")) if args.fwd_tiles else None
+    std_ws = None
+    if args.standard:
+        st, std_bytes = _lib.fa_std_workspace_size(B, H, N, d)
+        _lib.check(st, "fa_std_workspace_size")
+        std_ws = torch.empty(std_bytes, dtype=torch.uint8, device="cuda:0")
     names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if cfg["bwd"] else [])
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        if tiles is not None:
+        if std_ws is not None:
+            st = _lib.fa_std_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, N, d, causal, scale, mptr, std_ws.data_ptr(), std_ws.numel(), sptr)
+        elif tiles is not None:
             st = _lib.fa_fwd_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                    B, H, N, d, causal, scale, mptr, tiles[0], tiles[1], sptr)
         elif mptr is None:
@@ -281,7 +294,8 @@ def main(argv=None):
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                    "block_sparse": cfg["sparse"], "pass": "fwd+bwd" if cfg["bwd"] else "fwd",
                    "seed": args.seed, "parallelism": "single GPU",
-                   "fwd_tiles": list(tiles) if tiles else [128, 64]},
+                   "fwd_tiles": list(tiles) if tiles else [128, 64],
+                   "impl": "standard (materialised S)" if args.standard else "io-aware"},
         "frac_peak": round(value / PEAK_TFLOPS, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_TFLOPS, 4),
@@ -291,6 +305,8 @@ def main(argv=None):
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
         "roofline": roofline,
     }
+    if std_ws is not None:
+        out["workspace_bytes"] = std_ws.numel()
     if cfg["sparse"]:
         out["dense_equivalent_flops_per_step"] = fwd_flops(dict(cfg), None) * (3.5 if cfg["bwd"] else 1.0)
     if not args.no_cpu_baseline:

@@ -12,6 +12,10 @@ namespace fa {
 hipError_t launch_fwd(const FwdParams& p, int BH, int d, int bm, int bn, bool causal, bool sparse, bool debug,
                       hipStream_t st);
 bool fwd_config_supported(int bm, int bn);
+size_t std_workspace_bytes(int B, int H, int N);
+int std_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int H, int N,
+            int d, bool causal, float scale, const uint8_t* mask, void* workspace, hipStream_t st);
+constexpr int kStdMaxN = 16384;
 hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
                       hipStream_t st);
 }  // namespace fa
@@ -131,6 +135,30 @@ int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* ls
                   bm, bn);
 }
 
+int fa_std_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, 1.0f);
+  if (st != FA_OK) return st;
+  if (N > fa::kStdMaxN) return FA_ERR_SHAPE;
+  *bytes = fa::std_workspace_bytes(B, H, N);
+  return FA_OK;
+}
+
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, const uint8_t* block_mask, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (N > fa::kStdMaxN) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < fa::std_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace)) return FA_ERR_ALIGN;
+  const int r = fa::std_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d, causal != 0,
+                            scale, block_mask, workspace, (hipStream_t)stream);
+  return r == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {
   if (!bytes) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, 1.0f);
@@ -196,7 +224,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
     case FA_ERR_MASK: return "FA_ERR_MASK: block-sparse call without a block mask";
-    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch or rocBLAS call failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: device pointers must be 16-byte aligned";
     default: return "unknown fa status";
   }

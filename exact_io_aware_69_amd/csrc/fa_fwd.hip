@@ -38,7 +38,8 @@
 namespace fa {
 
 template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
+// Two 4-wave workgroups per CU unless the two K/V stages of one exceed half the LDS.
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static_assert(BN <= MASK_BLOCK && BM <= 2 * MASK_BLOCK, "a tile spans at most one mask column, two mask rows");
   constexpr int TILEB = BN * D * 2;

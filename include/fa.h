@@ -34,7 +34,7 @@
  *     on the host. Outputs must not alias inputs.
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     backward workspace. The library keeps no device memory and no global
- *     state between calls.
+ *     state between calls (fa_std_fwd aside: it keeps a rocBLAS handle).
  *   - Errors: every entry point returns FA_OK (0) or a negative fa_status.
  *     Argument checks run before anything is enqueued; a failed launch is
  *     reported as FA_ERR_HIP. Faults during execution surface at the
@@ -60,7 +60,7 @@ typedef enum fa_status {
     FA_ERR_SCALE = -4,          /* scale not finite or <= 0 */
     FA_ERR_WORKSPACE = -5,      /* backward workspace missing or too small */
     FA_ERR_MASK = -6,           /* block_mask NULL in a block-sparse call */
-    FA_ERR_HIP = -7,            /* a HIP launch or runtime call failed */
+    FA_ERR_HIP = -7,            /* a HIP launch, runtime or rocBLAS call failed */
     FA_ERR_ALIGN = -8           /* a pointer is not 16-byte aligned */
 } fa_status;
 
@@ -89,6 +89,22 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
 int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float scale,
                  const uint8_t* block_mask, int bm, int bn, void* stream);
+
+/* Standard attention, for comparison: the computation FlashAttention
+ * replaces, with the N x N score matrix written to and read back from device
+ * memory (Stanford FlashAttention summary, the paragraph on reads and writes
+ * of the attention matrix; FlashAttention-2 review, Abstract: memory
+ * quadratic in sequence length). Same arguments, results and conventions as
+ * fa_fwd_blocksparse (block_mask may be NULL for dense), plus a workspace of
+ * fa_std_workspace_size bytes (fp32 S and bf16 P, 6 * B * H * N * N bytes).
+ * S = Q K^T * scale and O = P V are rocBLAS strided-batched GEMMs (bf16
+ * operands, fp32 accumulation); masking and the row softmax are a HIP kernel.
+ * N <= 16384. The library keeps one rocBLAS handle per device for the life
+ * of the process. Library failures are reported as FA_ERR_HIP. */
+int fa_std_workspace_size(int B, int H, int N, int d, size_t* bytes);
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale,
+               const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need:
  * float32 D = rowsum(dO * O) for every row, O(B*H*N) -- never O(N^2). */

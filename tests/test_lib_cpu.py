@@ -159,3 +159,17 @@ def test_expected_visits_blocksparse():
 def test_fwd_tiles_rejects_unsupported_configs_before_launch():
     for bm, bn in [(64, 64), (256, 32), (128, 256), (512, 64), (0, 0)]:
         assert _lib.fa_fwd_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0, 0.125, None, bm, bn, None) == -2
+
+
+def test_std_fwd_argument_errors():
+    st, need = _lib.fa_std_workspace_size(1, 2, 256, 64)
+    assert st == 0 and need >= 2 * 256 * 256 * 6
+    assert _lib.fa_std_workspace_size(1, 1, 16385, 64)[0] == -2          # N above the baseline's limit
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=256, d=64, causal=0, scale=0.125,
+                block_mask=None, workspace=FAKE, workspace_bytes=need, stream=None)
+    assert _lib.fa_std_fwd(**{**args, "workspace_bytes": need - 1}) == -5
+    assert _lib.fa_std_fwd(**{**args, "workspace": None}) == -5
+    assert _lib.fa_std_fwd(**{**args, "q": None}) == -1
+    assert _lib.fa_std_fwd(**{**args, "d": 96}) == -3
+    assert _lib.fa_std_fwd(**{**args, "N": 16385}) == -2
+    assert _lib.fa_std_fwd(**{**args, "o": FAKE + 2}) == -8
