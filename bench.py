@@ -163,6 +163,11 @@ def main(argv=None):
     ap.add_argument("--standard", action="store_true",
                     help="time the standard attention baseline (materialised S; fa_std_fwd) instead of the "
                          "IO-aware forward; forward only")
+    ap.add_argument("--fa1", action="store_true",
+                    help="time the FlashAttention-1-style forward (fa_fwd_fa1; ablation) instead of the "
+                         "IO-aware forward; forward only, dense or causal")
+    ap.add_argument("--fa1-seq-groups", type=int, default=1, metavar="G",
+                    help="with --fa1: query-tile groups per head (1 = the published one workgroup per head)")
     ap.add_argument("--fwd-tiles", default=None, metavar="BM,BN",
                     help="run the forward through fa_fwd_tiles with this tile configuration (tile-size study)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -191,8 +196,11 @@ def main(argv=None):
 
     _lib.lib()  # raises if libfa.so is missing: there is no other path
     cfg = dict(WORKLOADS[args.workload])
-    if args.standard:
+    if args.standard or args.fa1:
         cfg["bwd"] = False
+    if args.fa1 and cfg["sparse"]:
+        print("--fa1 runs dense or causal attention only", file=sys.stderr)
+        return 2
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     scale = 1.0 / math.sqrt(d)
     inp = make_inputs(args.seed, B, H, N, d, with_do=cfg["bwd"], sparse=cfg["sparse"])
@@ -214,6 +222,11 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     tiles = tuple(int(x) for x in args.fwd_tiles.split(",")) if args.fwd_tiles else None
+    fa1_ws = None
+    if args.fa1:
+        st, fa1_bytes = _lib.fa_fa1_workspace_size(B, H, N, d)
+        _lib.check(st, "fa_fa1_workspace_size")
+        fa1_ws = torch.empty(fa1_bytes, dtype=torch.uint8, device="cuda:0")
     std_ws = None
     if args.standard:
         st, std_bytes = _lib.fa_std_workspace_size(B, H, N, d)
@@ -224,7 +237,11 @@ def main(argv=None):
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        if std_ws is not None:
+        if fa1_ws is not None:
+            st = _lib.fa_fwd_fa1(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, N, d, causal, scale, args.fa1_seq_groups, fa1_ws.data_ptr(), fa1_ws.numel(),
+                                 sptr)
+        elif std_ws is not None:
             st = _lib.fa_std_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                  B, H, N, d, causal, scale, mptr, std_ws.data_ptr(), std_ws.numel(), sptr)
         elif tiles is not None:
@@ -274,7 +291,9 @@ def main(argv=None):
     roofline = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-        "traffic": load_traffic(args.workload, dom), "avg_ms": round(kern_ms[dom], 4),
+        # counters were taken for the default kernels only
+        "traffic": None if (args.standard or args.fa1 or tiles) else load_traffic(args.workload, dom),
+        "avg_ms": round(kern_ms[dom], 4),
         "flops_per_launch": kern_flops[dom],
     }
     fwd_tf = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
@@ -295,7 +314,9 @@ def main(argv=None):
                    "block_sparse": cfg["sparse"], "pass": "fwd+bwd" if cfg["bwd"] else "fwd",
                    "seed": args.seed, "parallelism": "single GPU",
                    "fwd_tiles": list(tiles) if tiles else [128, 64],
-                   "impl": "standard (materialised S)" if args.standard else "io-aware"},
+                   **({"fa1_seq_groups": args.fa1_seq_groups} if args.fa1 else {}),
+                   "impl": ("standard (materialised S)" if args.standard else
+                            "flashattention-1-style (ablation)" if args.fa1 else "io-aware")},
         "frac_peak": round(value / PEAK_TFLOPS, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_TFLOPS, 4),
@@ -307,6 +328,8 @@ def main(argv=None):
     }
     if std_ws is not None:
         out["workspace_bytes"] = std_ws.numel()
+    if fa1_ws is not None:
+        out["workspace_bytes"] = fa1_ws.numel()
     if cfg["sparse"]:
         out["dense_equivalent_flops_per_step"] = fwd_flops(dict(cfg), None) * (3.5 if cfg["bwd"] else 1.0)
     if not args.no_cpu_baseline:

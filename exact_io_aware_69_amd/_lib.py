@@ -26,6 +26,8 @@ SIGNATURES = {
     "fa_fwd_tiles": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _i, _p]),
     "fa_std_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fa_std_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
+    "fa_fa1_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fa_fwd_fa1": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
     "fa_bwd_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
@@ -95,6 +97,18 @@ def fa_std_workspace_size(B, H, N, d):
 def fa_std_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, workspace, workspace_bytes, stream):
     return lib().fa_std_fwd(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, workspace,
                             workspace_bytes, stream)
+
+
+def fa_fa1_workspace_size(B, H, N, d):
+    """Returns (status, bytes)."""
+    out = _sz(0)
+    st = lib().fa_fa1_workspace_size(B, H, N, d, ctypes.byref(out))
+    return st, out.value
+
+
+def fa_fwd_fa1(q, k, v, o, lse, B, H, N, d, causal, scale, seq_groups, workspace, workspace_bytes, stream):
+    return lib().fa_fwd_fa1(q, k, v, o, lse, B, H, N, d, int(causal), scale, seq_groups, workspace, workspace_bytes,
+                            stream)
 
 
 def fa_bwd_workspace_size(B, H, N, d):

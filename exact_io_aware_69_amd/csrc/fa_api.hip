@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/fa.h"
@@ -16,6 +18,9 @@ size_t std_workspace_bytes(int B, int H, int N);
 int std_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int H, int N,
             int d, bool causal, float scale, const uint8_t* mask, void* workspace, hipStream_t st);
 constexpr int kStdMaxN = 16384;
+size_t fa1_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_fa1(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B, int H,
+                      int N, int d, bool causal, float scale, int groups, void* workspace, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
                       hipStream_t st);
 }  // namespace fa
@@ -157,6 +162,28 @@ int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d, causal != 0,
                             scale, block_mask, workspace, (hipStream_t)stream);
   return r == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fa1_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, 1.0f);
+  if (st != FA_OK) return st;
+  *bytes = fa::fa1_workspace_bytes(B, H, N, d);
+  return FA_OK;
+}
+
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, int seq_groups, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (seq_groups < 1 || (long long)B * H * std::min(seq_groups, (N + 31) / 32) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < fa::fa1_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace)) return FA_ERR_ALIGN;
+  const hipError_t e = fa::launch_fa1(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d,
+                                      causal != 0, scale, seq_groups, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {

@@ -106,6 +106,30 @@ int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale,
                const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream);
 
+/* FlashAttention-1-style forward, kept as a measured ablation of the
+ * FlashAttention-2 changes (FlashAttention-2 review, Abstract items (1)-(3)
+ * and "Research questions", RQ2): one workgroup per (batch, head) with no
+ * parallelism over sequence length; K/V tiles in the outer loop and query
+ * tiles in the inner loop, the running output, max and sum of every row
+ * kept in a device workspace and read and written back once per K/V tile;
+ * the keys of a tile split across the waves, combined through LDS; the
+ * output normalised after every tile. Same arguments and results as fa_fwd
+ * (no block mask), plus:
+ *   seq_groups  1 reproduces the published partitioning (B*H workgroups).
+ *               G > 1 deals the head's 32-row query tiles round-robin to G
+ *               workgroups per head (clamped to ceil(N/32)), adding only the
+ *               sequence parallelism of FlashAttention-2, so that its effect
+ *               is measured apart from the other two changes. < 1:
+ *               FA_ERR_SHAPE.
+ *   workspace   fa_fa1_workspace_size bytes of device memory, 16-byte
+ *               aligned, owned by the caller (fp32 output and per-wave
+ *               max/sum rows, linear in N); too small or NULL:
+ *               FA_ERR_WORKSPACE. Contents on entry are ignored. */
+int fa_fa1_workspace_size(int B, int H, int N, int d, size_t* bytes);
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, int seq_groups,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need:
  * float32 D = rowsum(dO * O) for every row, O(B*H*N) -- never O(N^2). */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);

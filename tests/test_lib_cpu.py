@@ -173,3 +173,19 @@ def test_std_fwd_argument_errors():
     assert _lib.fa_std_fwd(**{**args, "d": 96}) == -3
     assert _lib.fa_std_fwd(**{**args, "N": 16385}) == -2
     assert _lib.fa_std_fwd(**{**args, "o": FAKE + 2}) == -8
+
+
+def test_fa1_fwd_argument_errors():
+    st, need = _lib.fa_fa1_workspace_size(2, 3, 300, 128)
+    # fp32 output rows plus 4 per-wave (max, sum) pairs per row, linear in N
+    assert st == 0 and need >= 2 * 3 * 300 * (128 + 8) * 4 and need < 2 * 3 * 300 * (128 + 8) * 4 + 768
+    assert _lib.fa_fa1_workspace_size(1, 1, 0, 64)[0] == -2
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=3, N=300, d=128, causal=1, scale=0.125,
+                seq_groups=1, workspace=FAKE, workspace_bytes=need, stream=None)
+    assert _lib.fa_fwd_fa1(**{**args, "seq_groups": 0}) == -2
+    assert _lib.fa_fwd_fa1(**{**args, "workspace_bytes": need - 1}) == -5
+    assert _lib.fa_fwd_fa1(**{**args, "workspace": None}) == -5
+    assert _lib.fa_fwd_fa1(**{**args, "lse": None}) == -1
+    assert _lib.fa_fwd_fa1(**{**args, "d": 80}) == -3
+    assert _lib.fa_fwd_fa1(**{**args, "scale": 0.0}) == -4
+    assert _lib.fa_fwd_fa1(**{**args, "workspace": FAKE + 4}) == -8
