@@ -103,7 +103,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
-  p.Dvec = static_cast<float*>(workspace);
+  p.Dneg = static_cast<float*>(workspace);
   p.lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + workspace_half(B, H, N));
   p.mask = mask;
   p.visited_kv = visited_kv;

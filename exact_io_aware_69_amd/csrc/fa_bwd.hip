@@ -8,9 +8,9 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_k dO_ik O_ik,
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 // Three kernels, enqueued in order on one stream:
-//   1. fa_bwd_pre_kernel   per row: D = rowsum(dO o O) and lse * log2(e)
+//   1. fa_bwd_pre_kernel   per row: -D = -rowsum(dO o O) and lse * log2(e)
 //                          into the workspace, whose rows are padded per head
-//                          to a multiple of 128 (padding: D = 0, lse = +inf,
+//                          to a multiple of 128 (padding: -D = 0, lse = +inf,
 //                          so a padded or fully masked row has P = 0 without
 //                          any test in the hot loops);
 //   2. fa_bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile),
@@ -35,12 +35,12 @@
 
 namespace fa {
 
-// ------------------------------------------------------------------ D = rowsum(dO o O), lse * log2(e)
+// ------------------------------------------------------------------ -D = -rowsum(dO o O), lse * log2(e)
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dO,
                                                          const float* __restrict__ lse,
-                                                         float* __restrict__ Dvec, float* __restrict__ lse2,
+                                                         float* __restrict__ Dneg, float* __restrict__ lse2,
                                                          int N, int Npad, size_t rows_pad) {
   constexpr int CH = D / 8;      // lanes per row, 8 elements each
   constexpr int RPB = 256 / CH;  // rows per workgroup
@@ -68,43 +68,50 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
       const float l = lse[row];
       l2 = l == -INFINITY ? INFINITY : l * kLog2e;
     }
-    Dvec[prow] = acc;
+    Dneg[prow] = -acc;
     lse2[prow] = l2;
   }
 }
 
 // ------------------------------------------------------------------ dK, dV
 // A workgroup of 8 waves owns 128 keys. Waves w and w + 4 share keys
-// 32w .. 32w + 31 and split the four products of every query block evenly:
+// 32w .. 32w + 31 and split the four products of every query tile evenly:
 //   P-wave  (w < 4):  holds K; S = Q K^T, P = exp2(S*c - lse*log2e), passes
 //                     P (bf16) to its partner through LDS; dV^T += dO^T P.
-//   dS-wave (w >= 4): holds V; dP = dO V^T, reads P, dS = P o (dP - D);
-//                     dK^T += Q^T dS.
+//   dS-wave (w >= 4): holds V; dP - D = dO V^T - D (the product accumulates
+//                     onto -D), reads P, dS = P o (dP - D); dK^T += Q^T dS.
 // Each wave keeps one operand (32 keys x d) and one accumulator in
-// registers, so a SIMD runs one wave of each role and overlaps one's
-// vector work with the other's matrix products.
+// registers, so a SIMD runs one wave of each role.
+//
+// The query tiles are software-pipelined with one barrier per tile. In step
+// t the dS-wave forms dS of tile t-1 from its partner's P, runs tile t's dP
+// products, then tile t-1's dK products; the P-wave runs tile t-1's dV
+// products first, then tile t's S products and exponentials. The two waves
+// of a SIMD are thus out of phase: the products that read transposed
+// operands (limited by the LDS) overlap the products that read rows
+// (limited by the MFMA pipe). Three LDS stages rotate: tile t-1 (read by the
+// transposed products), tile t (row products) and tile t+1 (being copied);
+// each stage also holds its tile's P.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BNK = BWD_KV_BN;  // keys per workgroup
   constexpr int BMQ = BWD_KV_BM;  // query rows per streamed tile
   constexpr int QB = BMQ / 32;    // 32-query blocks per tile
   constexpr int TILEB = BMQ * D * 2;
+  constexpr int PXB = 4 * QB * 2048;  // P of a tile: [key group][query block][half][lane] x 16 bytes
   static_assert(BNK == MASK_BLOCK, "one key tile per mask column");
   static_assert(BMQ == 64, "lse/D rows are copied by one wave-wide 4-byte copy");
-  __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t o0_raw[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t o1_raw[TILEB];
-  __shared__ __attribute__((aligned(256))) float l0_raw[2 * BMQ];  // lse*log2e, then D
-  __shared__ __attribute__((aligned(256))) float l1_raw[2 * BMQ];
-  // P of every (key group, query block), in the MFMA result layout: lane l
-  // of key group kg stores its 16 values as two 16-byte halves at
-  // [kg][qb][half][l].
-  __shared__ __attribute__((aligned(1024))) uint8_t px_raw[4 * QB * 64 * 32];
-  FA_LDS uint8_t* const qst[2] = {(FA_LDS uint8_t*)q0_raw, (FA_LDS uint8_t*)q1_raw};
-  FA_LDS uint8_t* const ost[2] = {(FA_LDS uint8_t*)o0_raw, (FA_LDS uint8_t*)o1_raw};
-  FA_LDS float* const lst[2] = {(FA_LDS float*)l0_raw, (FA_LDS float*)l1_raw};
-  FA_LDS uint8_t* const px = (FA_LDS uint8_t*)px_raw;
+  // Three stages of each kind of data, one array per kind.
+  __shared__ __attribute__((aligned(1024))) uint8_t q_raw[3 * TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t o_raw[3 * TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t p_raw[3 * PXB];
+  __shared__ __attribute__((aligned(256))) float l_raw[3 * 2 * BMQ];  // per stage: lse*log2e rows, then -D rows
+  struct Stage {
+    FA_LDS uint8_t* q;   // Q tile
+    FA_LDS uint8_t* o;   // dO tile
+    FA_LDS float* l;     // lse*log2e rows; -D rows at l + BMQ
+    FA_LDS uint8_t* px;  // P of the tile
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h2 = lane >> 5;
@@ -146,141 +153,224 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
     return i;
   };
 
-  // Q, dO of this head and its lse*log2e / D rows as buffer resources. Rows
+  // Q, dO of this head and its lse*log2e / -D rows as buffer resources. Rows
   // past N read as zero; their lse is +inf in the padded workspace, so they
   // contribute P = 0.
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const uint32_t row_bytes = (uint32_t)p.Npad * 4;
   const float* l2g = p.lse2 + (size_t)bh * p.Npad;
-  const float* Dg = p.Dvec + (size_t)bh * p.Npad;
-  const TileDMA<D, BMQ, 8> cp(w, lane);
-  // Query tile i -> LDS: Q and dO rows, and the 64 lse*log2e and D values
-  // (waves 0 and 1, 4 bytes per lane).
-  auto dma_q = [&](int i, FA_LDS uint8_t* qdst, FA_LDS uint8_t* odst, FA_LDS float* ldst)
-                   __attribute__((always_inline)) {
-    cp.copy(p.q + head, head_bytes, i * BMQ * D * 2, qdst, w);
-    cp.copy(p.dO + head, head_bytes, i * BMQ * D * 2, odst, w);
-    if (w == 0) dma4(l2g, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)ldst);
-    if (w == 1) dma4(Dg, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)(ldst + BMQ));
+  const float* Dg = p.Dneg + (size_t)bh * p.Npad;
+  // The P-waves issue every tile copy: they wait at the barrier for their
+  // partners anyway, so the dS-waves never stall on the copy queue.
+  const TileDMA<D, BMQ, 4> cp(kg, lane);
+  auto dma_q = [&](int i, const Stage& sb) __attribute__((always_inline)) {  // P-waves only
+    cp.copy(p.q + head, head_bytes, i * BMQ * D * 2, sb.q, kg);
+    cp.copy(p.dO + head, head_bytes, i * BMQ * D * 2, sb.o, kg);
+    if (w == 0) dma4(l2g, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)sb.l);
+    if (w == 1) dma4(Dg, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)(sb.l + BMQ));
   };
 
   const float c = p.c;
+  const int hh = lane >> 5, g = lane >> 4, jj = lane & 15;
+  const int trow = 4 * hh + (jj >> 2);
+  const int tcol = 16 * (g & 1) + 4 * (jj & 3);
+  const int arow = lane & 31;
 
-  // Phase 1 of a tile: S (P-wave) or dP (dS-wave) for each query block; the
-  // P-wave turns S into bf16 P, keeps it and writes it for its partner.
-  // Phase 2 (after a barrier): dV^T += dO^T P or dK^T += Q^T dS.
-  auto tile = [&](int i, const FA_LDS uint8_t* qs, const FA_LDS uint8_t* dos, const FA_LDS float* ls,
-                  auto last) __attribute__((always_inline)) {
-    const int ln = lane;
-    const int hh = ln >> 5, g = ln >> 4, jj = ln & 15;
-    const int trow = 4 * hh + (jj >> 2);
-    const int tcol = 16 * (g & 1) + 4 * (jj & 3);
-    const int arow = ln & 31;
-    const FA_LDS uint8_t* a1 = dswave ? dos : qs;  // phase-1 A operand rows
-    const FA_LDS uint8_t* a2 = dswave ? qs : dos;  // phase-2 A operand (transposed)
-    f32x16 sd[QB];  // S or dP per query block
-    bf16x8 pb[QB][2];
-    bool live[QB];
+  f32x16 sd[QB];       // S (P-wave) or dP - D (dS-wave) of the current tile
+  bf16x8 pend[QB][2];  // P (P-wave) or dS (dS-wave) of the previous tile, B operand of its deferred product
+
+  // S^T = K Q^T (P-wave, from zero) or dP^T - D = V dO^T - D (dS-wave, from
+  // the -D rows) of tile i. Value r of block qb is query
+  // i*BMQ + 32*qb + 8*(r/4) + 4*hh + r%4, key `key`.
+  auto products_a = [&](auto role, int i, const Stage& sb) __attribute__((always_inline)) {
+    constexpr bool DSW = decltype(role)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const FA_LDS uint8_t* a1 = DSW ? sb.o : sb.q;
+    if (DEBUG && tid == 0) p.visited_kv[((size_t)bh * n_kt + jt) * n_qt + i] = 1;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qbase = i * BMQ + 32 * qb;
-      live[qb] = !(CAUSAL && qbase + 31 < k0w);  // false: every query precedes every key
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sd[qb][r] = 0.f;
-      if (live[qb]) {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          sd[qb] = mfma32(ld_lds16(a1, tile_off<D>(32 * qb + arow, 16 * kk + 8 * hh)), kvf[kk], sd[qb]);
-      }
-    }
-    if (!dswave) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (!live[qb]) continue;
-        const int qbase = i * BMQ + 32 * qb;
-        const bool need_mask = CAUSAL && (k0w + 31 > qbase);
-        // value r of this lane is query qbase + 8*(r/4) + 4*hh + r%4, key `key`
-        float pe[16];
+      if (DSW) {
+        const FA_LDS float* dl = sb.l + BMQ;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 32 * qb + 8 * rg + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pe[4 * rg + e] = fast_exp2(fmaf(sd[qb][4 * rg + e], c, -l4[e]));
+          for (int e = 0; e < 4; ++e) sd[qb][4 * rg + e] = d4[e];
         }
-        if (need_mask) {  // only blocks that straddle the diagonal
-          const int lim = key - qbase - 4 * hh;  // masked iff 8*(r/4) + r%4 < lim
+      } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) < lim) pe[r] = 0.f;
-        }
-        pb[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
-        pb[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
-        // Two 1 KiB halves, 16 bytes per lane in each (conflict-free).
-        FA_LDS uint8_t* dst = px + (kg * QB + qb) * 2048 + ln * 16;
-        *reinterpret_cast<FA_LDS bf16x8*>(dst) = pb[qb][0];
-        *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) = pb[qb][1];
+        for (int r = 0; r < 16; ++r) sd[qb][r] = 0.f;
       }
     }
-    __syncthreads();
-    if (dswave) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (!live[qb]) continue;
-        const FA_LDS uint8_t* src = px + (kg * QB + qb) * 2048 + ln * 16;
-        const bf16x8 p0 = *reinterpret_cast<const FA_LDS bf16x8*>(src);
-        const bf16x8 p1 = *reinterpret_cast<const FA_LDS bf16x8*>(src + 1024);
-        float ds[16];
+    for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + BMQ + 32 * qb + 8 * rg + 4 * hh);
+      for (int qb = 0; qb < QB; ++qb)
+        sd[qb] = mfma32(ld_lds16(a1, tile_off<D>(32 * qb + arow, 16 * kk + 8 * hh)), kvf[kk], sd[qb]);
+    // Issue order: the -D rows and the operands of the first two k-steps,
+    // then each k-step's products followed by the reads two k-steps ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, (DSW ? 4 * QB : 0) + 2 * QB, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            const float pv = (float)(r < 8 ? p0[r] : p1[r - 8]);
-            ds[r] = pv * (sd[qb][r] - d4[e]);
-          }
-        }
-        pb[qb][0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-        pb[qb][1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
-      }
+    for (int kk = 0; kk < D / 16 - 2; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, QB, 0);
     }
-    // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave); query slots of
-    // k-step ks are 16*ks + 8*(i/4) + 4*hh + i%4 on both operands.
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Causal mask of tile i on the P-wave's S: masked (S = -inf, so P = 0)
+  // where the query precedes the key. Only tiles that reach the diagonal
+  // need it; blocks wholly before the keys end up all zero.
+  auto causal_mask = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (!live[qb]) continue;
+      const int lim = key - (i * BMQ + 32 * qb) - 4 * hh;  // masked iff 8*(r/4) + r%4 < lim
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) < lim) sd[qb][r] = -INFINITY;
+    }
+  };
+  // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave) for the previous
+  // tile, whose rows are in stage sb; query slots of k-step ks are
+  // 16*ks + 8*(e/4) + 4*hh + e%4 on both operands.
+  auto products_b = [&](auto role, const Stage& sb) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    const FA_LDS uint8_t* a2 = decltype(role)::value ? sb.q : sb.o;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const int rr = 32 * qb + 16 * ks + trow;
           const int cc = 32 * dt + tcol;
           const bf16x8 aT = join_tr(ld_lds_tr(a2, tile_off<D>(rr, cc)), ld_lds_tr(a2, tile_off<D>(rr + 8, cc)));
-          acc[dt] = mfma32(aT, pb[qb][ks], acc[dt]);
+          acc[dt] = mfma32(aT, pend[qb][ks], acc[dt]);
         }
+    // Issue order: the reads of the first four products, then each product
+    // followed by the two reads of the product four places ahead.
+    constexpr int NM = QB * 2 * (D / 32);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int m = 0; m < NM - 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // P of the current tile (P-wave): bf16 into pnew and into the stage's P.
+  auto exp_p = [&](const Stage& sb, bf16x8 (&pnew)[QB][2]) __attribute__((always_inline)) {
+    const FA_LDS float* ls = sb.l;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float pe[16];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 32 * qb + 8 * rg + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[4 * rg + e] = fast_exp2(fmaf(sd[qb][4 * rg + e], c, -l4[e]));
       }
+      pnew[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+      pnew[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+      // Two 1 KiB halves, 16 bytes per lane in each (conflict-free).
+      FA_LDS uint8_t* dst = sb.px + (kg * QB + qb) * 2048 + lane * 16;
+      *reinterpret_cast<FA_LDS bf16x8*>(dst) = pnew[qb][0];
+      *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) = pnew[qb][1];
     }
   };
+  // dS of the previous tile (dS-wave) from its dP - D (sd) and the
+  // partner's P stored in that tile's stage.
+  auto form_ds = [&](const Stage& sb) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pp[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const FA_LDS uint8_t* src = sb.px + (kg * QB + qb) * 2048 + lane * 16;
+      pp[qb][0] = *reinterpret_cast<const FA_LDS bf16x8*>(src);
+      pp[qb][1] = *reinterpret_cast<const FA_LDS bf16x8*>(src + 1024);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pp[qb][0][r] : pp[qb][1][r - 8]) * sd[qb][r];
+      pend[qb][0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      pend[qb][1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * QB, 0);  // all P reads first
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto needs_mask = [&](int i) __attribute__((always_inline)) { return CAUSAL && k0w + 31 > i * BMQ; };
+  auto stage = [&](int S) __attribute__((always_inline)) {
+    return Stage{(FA_LDS uint8_t*)q_raw + S * TILEB, (FA_LDS uint8_t*)o_raw + S * TILEB,
+                 (FA_LDS float*)l_raw + S * 2 * BMQ, (FA_LDS uint8_t*)p_raw + S * PXB};
+  };
 
-  int ic = next_tile(it_begin);
-  if (ic < n_qt) {
-    dma_q(ic, qst[0], ost[0], lst[0]);
-    wait_vmem();
-    __syncthreads();
-    auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
-      constexpr int P = decltype(parity)::value;
+  // The whole sweep, instantiated once per role so that each role's
+  // loop-invariant addresses stay in its own branch. Both roles pass the
+  // same number of barriers.
+  auto sweep = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool DSW = decltype(role)::value;
+    int ic = next_tile(it_begin);
+    if (ic >= n_qt) return;
+    // The last tile's transposed products (its rows are in stage s).
+    auto tail = [&](int s) __attribute__((always_inline)) {
+      if (DSW) form_ds(stage(s));
+      products_b(role, stage(s));
+    };
+    // One step: tile ic in stage SC; the previous tile is in stage SP, the
+    // next one is copied into stage SN. Returns false after the last tile.
+    auto step = [&](int SC) __attribute__((always_inline)) -> bool {
+      const int SP = SC == 0 ? 2 : SC - 1, SN = SC == 2 ? 0 : SC + 1;
       const int in = next_tile(ic + 1);
-      if (in < n_qt) dma_q(in, qst[1 - P], ost[1 - P], lst[1 - P]);
-      if (DEBUG && tid == 0) p.visited_kv[((size_t)bh * n_kt + jt) * n_qt + ic] = 1;
-      tile(ic, qst[P], ost[P], lst[P], parity);
+      if (!DSW && in < n_qt) dma_q(in, stage(SN));
+      if (DSW) {
+        form_ds(stage(SP));
+        products_a(role, ic, stage(SC));
+        products_b(role, stage(SP));
+      } else {
+        // The opposite order to the dS-wave on the same SIMD: this wave's
+        // transposed products (bound by the transposing LDS reads) overlap
+        // its partner's row products (bound by the MFMA pipe), and the
+        // other way round.
+        products_b(role, stage(SP));
+        products_a(role, ic, stage(SC));
+        if (needs_mask(ic)) causal_mask(ic);
+        exp_p(stage(SC), pend);
+      }
       wait_vmem();
       __syncthreads();
       ic = in;
-      return in < n_qt;
+      if (ic < n_qt) return true;
+      tail(SC);
+      return false;
     };
-    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    // First tile (stage 0): its row products and P only.
+    if (!DSW) dma_q(ic, stage(0));
+    wait_vmem();
+    __syncthreads();
+    const int in = next_tile(ic + 1);
+    if (!DSW && in < n_qt) dma_q(in, stage(1));
+    products_a(role, ic, stage(0));
+    if (!DSW) {
+      if (needs_mask(ic)) causal_mask(ic);
+      exp_p(stage(0), pend);
     }
-  }
+    wait_vmem();
+    __syncthreads();
+    ic = in;
+    if (ic >= n_qt) {
+      tail(0);
+      return;
+    }
+    int sc = 1;
+    while (step(sc)) sc = sc == 2 ? 0 : sc + 1;
+  };
+  if (dswave)
+    sweep(std::true_type());
+  else
+    sweep(std::false_type());
 
   if (key < N) {
     uint16_t* dst = (dswave ? p.dk : p.dv) + head + (size_t)key * D;
@@ -348,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     }
   }
   const float lse2 = p.lse2[(size_t)bh * p.Npad + qi];
-  const float Dq = p.Dvec[(size_t)bh * p.Npad + qi];
+  const float Dq = p.Dneg[(size_t)bh * p.Npad + qi];  // -D of this lane's query
   f32x16 dqt[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -410,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
       }
       bf16x8 dsb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)(pe[i] * (dp[mt][r0 + i] - Dq));
+      for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)(pe[i] * (dp[mt][r0 + i] + Dq));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int rr = 16 * kk + trow;
@@ -467,7 +557,7 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
     const size_t rows_pad = (size_t)BH * p.Npad;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
-                       p.dO, p.lse, p.Dvec, p.lse2, p.N, p.Npad, rows_pad);
+                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -49,7 +49,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   const float* lse;  // forward's lse, [B*H*N]
-  float* Dvec;       // workspace: rowsum(dO * O), [B*H][Npad]
+  float* Dneg;       // workspace: -rowsum(dO * O), [B*H][Npad]
   float* lse2;       // workspace: lse * log2(e) (+inf for no visible key or padding), [B*H][Npad]
   const uint8_t* mask;
   uint8_t* visited_kv;  // [B*H][n_kt1][n_qt1] or nullptr
