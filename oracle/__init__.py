@@ -6,7 +6,9 @@ and shares no code with it.
 
 Everything here is the plain definition of scaled-dot-product attention and
 its analytic gradient, evaluated in float64 over the bf16 input bits
-(see ``oracle.attention`` for the passages each function follows).
+(see ``oracle.attention`` for the passages each function follows), and in
+``oracle.dropout`` the same with attention dropout (a Philox4x32-10 keep
+mask on the probabilities).
 """
 from .attention import (  # noqa: F401
     widen_bf16,
