@@ -166,6 +166,9 @@ def main(argv=None):
     ap.add_argument("--fa1", action="store_true",
                     help="time the FlashAttention-1-style forward (fa_fwd_fa1; ablation) instead of the "
                          "IO-aware forward; forward only, dense or causal")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="attention dropout probability (fa_fwd_dropout / fa_bwd_dropout; the backward is timed "
+                         "as one call)")
     ap.add_argument("--fa1-seq-groups", type=int, default=1, metavar="G",
                     help="with --fa1: query-tile groups per head (1 = the published one workgroup per head)")
     ap.add_argument("--fwd-tiles", default=None, metavar="BM,BN",
@@ -232,12 +235,22 @@ def main(argv=None):
         st, std_bytes = _lib.fa_std_workspace_size(B, H, N, d)
         _lib.check(st, "fa_std_workspace_size")
         std_ws = torch.empty(std_bytes, dtype=torch.uint8, device="cuda:0")
-    names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if cfg["bwd"] else [])
+    drop = args.dropout > 0
+    if drop and (args.standard or args.fa1 or tiles is not None):
+        print("--dropout runs the IO-aware kernels with the default tiles only", file=sys.stderr)
+        return 2
+    if drop:
+        names = ["fwd"] + (["bwd"] if cfg["bwd"] else [])
+    else:
+        names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if cfg["bwd"] else [])
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        if fa1_ws is not None:
+        if drop:
+            st = _lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     B, H, N, d, causal, scale, mptr, args.dropout, args.seed, 0, sptr)
+        elif fa1_ws is not None:
             st = _lib.fa_fwd_fa1(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                  B, H, N, d, causal, scale, args.fa1_seq_groups, fa1_ws.data_ptr(), fa1_ws.numel(),
                                  sptr)
@@ -256,7 +269,14 @@ def main(argv=None):
         _lib.check(st, "fa_fwd")
         if events is not None:
             events[1].record(stream)
-        if cfg["bwd"]:
+        if cfg["bwd"] and drop:
+            st = _lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal,
+                                     scale, mptr, args.dropout, args.seed, 0, ws.data_ptr(), ws_bytes, sptr)
+            _lib.check(st, "fa_bwd_dropout")
+            if events is not None:
+                events[2].record(stream)
+        elif cfg["bwd"]:
             for stage in range(3):
                 st = _lib.fa_bwd_stage(stage, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -285,14 +305,14 @@ def main(argv=None):
     # Algorithmic FLOPs attributed to each kernel: the forward's two GEMMs;
     # the dK/dV kernel's four of the backward's five GEMMs (S, dP, dV, dK);
     # the dQ kernel's dQ GEMM (its S and dP recomputation is not counted).
-    kern_flops = {"fwd": f_fwd, "bwd_pre": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd}
+    kern_flops = {"fwd": f_fwd, "bwd_pre": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd, "bwd": 2.5 * f_fwd}
     dom = max(names, key=lambda n: kern_ms[n])
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roofline = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
         # counters were taken for the default kernels only
-        "traffic": None if (args.standard or args.fa1 or tiles) else load_traffic(args.workload, dom),
+        "traffic": None if (args.standard or args.fa1 or tiles or drop) else load_traffic(args.workload, dom),
         "avg_ms": round(kern_ms[dom], 4),
         "flops_per_launch": kern_flops[dom],
     }
@@ -315,6 +335,7 @@ def main(argv=None):
                    "seed": args.seed, "parallelism": "single GPU",
                    "fwd_tiles": list(tiles) if tiles else [128, 64],
                    **({"fa1_seq_groups": args.fa1_seq_groups} if args.fa1 else {}),
+                   **({"dropout_p": args.dropout} if drop else {}),
                    "impl": ("standard (materialised S)" if args.standard else
                             "flashattention-1-style (ablation)" if args.fa1 else "io-aware")},
         "frac_peak": round(value / PEAK_TFLOPS, 4),

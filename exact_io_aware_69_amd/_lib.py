@@ -18,6 +18,8 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
+_u32 = ctypes.c_uint32
+_u64 = ctypes.c_uint64
 
 # name -> (restype, argtypes); mirrors include/fa.h
 SIGNATURES = {
@@ -32,6 +34,10 @@ SIGNATURES = {
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
     "fa_bwd_stage": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
+    "fa_fwd_dropout": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _f, _u64, _u32, _p]),
+    "fa_bwd_dropout": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _f, _u64, _u32, _p, _sz,
+                            _p]),
+    "fa_dropout_keep": (_i, [_i, _i, _i, _f, _u64, _u32, _p, _p]),
     "fa_tile_config": (_i, [_i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "fa_fwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p]),
     "fa_bwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz,
@@ -42,7 +48,7 @@ SIGNATURES = {
 FA_OK = 0
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED_D", -4: "FA_ERR_SCALE",
-    -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_MASK", -7: "FA_ERR_HIP", -8: "FA_ERR_ALIGN",
+    -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_MASK", -7: "FA_ERR_HIP", -8: "FA_ERR_ALIGN", -9: "FA_ERR_DROPOUT",
 }
 
 
@@ -133,6 +139,21 @@ def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, sca
                  workspace_bytes, stream):
     return lib().fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale, block_mask,
                               workspace, workspace_bytes, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, dropout_p, seed, offset, stream):
+    return lib().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, int(causal), scale, block_mask, dropout_p, seed, offset,
+                                stream)
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, dropout_p, seed, offset,
+                   workspace, workspace_bytes, stream):
+    return lib().fa_bwd_dropout(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale, block_mask,
+                                dropout_p, seed, offset, workspace, workspace_bytes, stream)
+
+
+def fa_dropout_keep(B, H, N, dropout_p, seed, offset, keep, stream):
+    return lib().fa_dropout_keep(B, H, N, dropout_p, seed, offset, keep, stream)
 
 
 def fa_tile_config(pass_, d):

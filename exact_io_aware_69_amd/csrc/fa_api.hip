@@ -23,6 +23,10 @@ hipError_t launch_fa1(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
                       int N, int d, bool causal, float scale, int groups, void* workspace, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool sparse, bool debug, int stages,
                       hipStream_t st);
+hipError_t launch_fwd_dropout(const FwdParams& p, int BH, int d, bool causal, bool sparse, hipStream_t st);
+hipError_t launch_bwd_dropout(const BwdParams& p, int BH, int d, bool causal, bool sparse, int stages,
+                              hipStream_t st);
+hipError_t launch_dropout_keep(uint8_t* keep, int BH, int N, const Dropout& dr, hipStream_t st);
 }  // namespace fa
 
 namespace {
@@ -53,9 +57,20 @@ size_t workspace_half(int B, int H, int N) {
 }
 size_t workspace_bytes_for(int B, int H, int N) { return 2 * workspace_half(B, H, N); }
 
+// Dropout arguments -> generator parameters; p must lie in [0, 1).
+int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* dr) {
+  if (!(p >= 0.f) || !(p < 1.f)) return FA_ERR_DROPOUT;
+  dr->t = (uint32_t)std::min(floor((double)p * 4294967296.0), 4294967295.0);
+  dr->k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  dr->k1 = (uint32_t)(seed >> 32);
+  dr->off = offset;
+  dr->scale = (float)(1.0 / (1.0 - (double)p));
+  return FA_OK;
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
              int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream,
-             int bm = fa::FWD_BM, int bn = fa::FWD_BN) {
+             int bm = fa::FWD_BM, int bn = fa::FWD_BN, const fa::Dropout* drop = nullptr) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale);
   if (st != FA_OK) return st;
@@ -75,15 +90,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.n_kt = (N + bn - 1) / bn;
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
-  hipError_t e =
-      fa::launch_fwd(p, B * H, d, bm, bn, causal != 0, sparse, visited != nullptr, (hipStream_t)stream);
+  p.drop = drop ? *drop : fa::Dropout{0, 0, 0, 0, 1.0f};
+  hipError_t e = drop ? fa::launch_fwd_dropout(p, B * H, d, causal != 0, sparse, (hipStream_t)stream)
+                      : fa::launch_fwd(p, B * H, d, bm, bn, causal != 0, sparse, visited != nullptr,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
              void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
              const uint8_t* mask, bool sparse, void* workspace, size_t workspace_bytes, uint8_t* visited_kv,
-             uint8_t* visited_q, int stages, void* stream) {
+             uint8_t* visited_q, int stages, void* stream, const fa::Dropout* drop = nullptr, float dropout_p = 0.f) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale);
   if (st != FA_OK) return st;
@@ -114,8 +131,11 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
-  hipError_t e =
-      fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, stages, (hipStream_t)stream);
+  p.dfac = drop ? (float)(1.0 - (double)dropout_p) : 1.0f;
+  p.drop = drop ? *drop : fa::Dropout{0, 0, 0, 0, 1.0f};
+  hipError_t e = drop ? fa::launch_bwd_dropout(p, B * H, d, causal != 0, sparse, stages, (hipStream_t)stream)
+                      : fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, stages,
+                                       (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -216,6 +236,39 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                   workspace, workspace_bytes, nullptr, nullptr, 1 << stage, stream);
 }
 
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   int causal, float scale, const uint8_t* block_mask, float dropout_p, uint64_t seed,
+                   uint32_t offset, void* stream) {
+  fa::Dropout dr;
+  const int st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, block_mask != nullptr, nullptr, stream,
+                  fa::FWD_BM, fa::FWD_BN, &dr);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                   const uint8_t* block_mask, float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  fa::Dropout dr;
+  const int st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, block_mask != nullptr,
+                  workspace, workspace_bytes, nullptr, nullptr, 7, stream, &dr, dropout_p);
+}
+
+int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset, uint8_t* keep,
+                    void* stream) {
+  if (!keep) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FA_ERR_SHAPE;
+  if ((long long)B * H * N * ((N + 3) / 4) / 256 >= 0x7fffffffLL) return FA_ERR_SHAPE;
+  fa::Dropout dr;
+  const int st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  const hipError_t e = fa::launch_dropout_keep(keep, B * H, N, dr, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_tile_config(int pass, int d, int* bm, int* bn) {
   if (!bm || !bn) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
@@ -253,6 +306,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_MASK: return "FA_ERR_MASK: block-sparse call without a block mask";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch or rocBLAS call failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: device pointers must be 16-byte aligned";
+    case FA_ERR_DROPOUT: return "FA_ERR_DROPOUT: dropout probability must be in [0, 1)";
     default: return "unknown fa status";
   }
 }

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ dO,
                                                          const float* __restrict__ lse,
                                                          float* __restrict__ Dneg, float* __restrict__ lse2,
-                                                         int N, int Npad, size_t rows_pad) {
+                                                         int N, int Npad, size_t rows_pad, float dfac) {
   constexpr int CH = D / 8;      // lanes per row, 8 elements each
   constexpr int RPB = 256 / CH;  // rows per workgroup
   const size_t prow = (size_t)blockIdx.x * RPB + threadIdx.x / CH;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
       const float l = lse[row];
       l2 = l == -INFINITY ? INFINITY : l * kLog2e;
     }
-    Dneg[prow] = -acc;
+    Dneg[prow] = -acc * dfac;
     lse2[prow] = l2;
   }
 }
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
 // (limited by the MFMA pipe). Three LDS stages rotate: tile t-1 (read by the
 // transposed products), tile t (row products) and tile t+1 (being copied);
 // each stage also holds its tile's P.
-template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BNK = BWD_KV_BN;  // keys per workgroup
   constexpr int BMQ = BWD_KV_BM;  // query rows per streamed tile
@@ -260,7 +260,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
     __builtin_amdgcn_sched_barrier(0);
   };
   // P of the current tile (P-wave): bf16 into pnew and into the stage's P.
-  auto exp_p = [&](const Stage& sb, bf16x8 (&pnew)[QB][2]) __attribute__((always_inline)) {
+  // With dropout, P keeps its sign where the key is kept and is negated
+  // where it is dropped in the copy for the partner (so the keep bit travels
+  // with it), and the dV operand is P on kept entries, 0 elsewhere.
+  auto exp_p = [&](int i, const Stage& sb, bf16x8 (&pnew)[QB][2]) __attribute__((always_inline)) {
     const FA_LDS float* ls = sb.l;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -271,12 +274,38 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) pe[4 * rg + e] = fast_exp2(fmaf(sd[qb][4 * rg + e], c, -l4[e]));
       }
+      FA_LDS uint8_t* dst = sb.px + (kg * QB + qb) * 2048 + lane * 16;
+      if (DROP) {
+        // Values 4*rg .. 4*rg+3 are queries i0 .. i0+3 at this lane's key.
+        // The quad of lanes holding keys 4m .. 4m+3 makes the four
+        // generator calls of the 4 x 4 block (lane t: query i0 + t, four
+        // keys) and transposes the words so each lane gets its own key.
+        float px[16];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int i0 = i * BMQ + 32 * qb + 8 * rg + 4 * hh;
+          uint32_t wv[4];
+          philox4x32_10((uint32_t)key >> 2, (uint32_t)(i0 + (lane & 3)), (uint32_t)bh, p.drop.off, p.drop.k0,
+                        p.drop.k1, wv);
+          quad_transpose4(wv, lane & 3);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool kept = wv[e] >= p.drop.t;
+            px[4 * rg + e] = kept ? pe[4 * rg + e] : -pe[4 * rg + e];
+            pe[4 * rg + e] = kept ? pe[4 * rg + e] : 0.f;
+          }
+        }
+        *reinterpret_cast<FA_LDS bf16x8*>(dst) = to_bf16x8(px[0], px[1], px[2], px[3], px[4], px[5], px[6], px[7]);
+        *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) =
+            to_bf16x8(px[8], px[9], px[10], px[11], px[12], px[13], px[14], px[15]);
+      }
       pnew[qb][0] = to_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
       pnew[qb][1] = to_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
-      // Two 1 KiB halves, 16 bytes per lane in each (conflict-free).
-      FA_LDS uint8_t* dst = sb.px + (kg * QB + qb) * 2048 + lane * 16;
-      *reinterpret_cast<FA_LDS bf16x8*>(dst) = pnew[qb][0];
-      *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) = pnew[qb][1];
+      if (!DROP) {
+        // Two 1 KiB halves, 16 bytes per lane in each (conflict-free).
+        *reinterpret_cast<FA_LDS bf16x8*>(dst) = pnew[qb][0];
+        *reinterpret_cast<FA_LDS bf16x8*>(dst + 1024) = pnew[qb][1];
+      }
     }
   };
   // dS of the previous tile (dS-wave) from its dP - D (sd) and the
@@ -293,8 +322,24 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float ds[16];
+      if (DROP) {
+        // Kept (P >= 0): dS = P (dP - D) with dP, D both in units of
+        // 1 - p; dropped (P stored negated): dS = -P D = P' * D.
+        const FA_LDS float* dl = sb.l + BMQ;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pp[qb][0][r] : pp[qb][1][r - 8]) * sd[qb][r];
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            const float pv = (float)(r < 8 ? pp[qb][0][r] : pp[qb][1][r - 8]);
+            ds[r] = pv * (pv >= 0.f ? sd[qb][r] : -d4[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pp[qb][0][r] : pp[qb][1][r - 8]) * sd[qb][r];
+      }
       pend[qb][0] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       pend[qb][1] = to_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
     }
@@ -337,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
         products_b(role, stage(SP));
         products_a(role, ic, stage(SC));
         if (needs_mask(ic)) causal_mask(ic);
-        exp_p(stage(SC), pend);
+        exp_p(ic, stage(SC), pend);
       }
       wait_vmem();
       __syncthreads();
@@ -355,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
     products_a(role, ic, stage(0));
     if (!DSW) {
       if (needs_mask(ic)) causal_mask(ic);
-      exp_p(stage(0), pend);
+      exp_p(ic, stage(0), pend);
     }
     wait_vmem();
     __syncthreads();
@@ -374,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 
   if (key < N) {
     uint16_t* dst = (dswave ? p.dk : p.dv) + head + (size_t)key * D;
-    const float sc = dswave ? p.scale : 1.0f;
+    const float sc = (dswave ? p.scale : 1.0f) * (DROP ? p.drop.scale : 1.0f);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -387,7 +432,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 }
 
 // ------------------------------------------------------------------ dQ
-template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = BWD_Q_BM;
   constexpr int BN = bwd_q_bn<D>();
@@ -499,8 +544,22 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
         }
       }
       bf16x8 dsb;
+      if (DROP) {
+        // Slots 0-3 are keys kd .. kd+3, slots 4-7 keys kd+8 .. kd+11. Kept:
+        // dS = P (dP - D); dropped: dS = -P D (dP and D in units of 1 - p).
+        const int kd = kbase + 16 * kk + 4 * h2;
+        uint32_t w0[4], w1[4];
+        philox4x32_10((uint32_t)kd >> 2, (uint32_t)qi, (uint32_t)bh, p.drop.off, p.drop.k0, p.drop.k1, w0);
+        philox4x32_10((uint32_t)(kd + 8) >> 2, (uint32_t)qi, (uint32_t)bh, p.drop.off, p.drop.k0, p.drop.k1, w1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)(pe[i] * (dp[mt][r0 + i] + Dq));
+        for (int i = 0; i < 8; ++i) {
+          const bool kept = (i < 4 ? w0[i] : w1[i - 4]) >= p.drop.t;
+          dsb[i] = (__bf16)(pe[i] * ((kept ? dp[mt][r0 + i] : 0.f) + Dq));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsb[i] = (__bf16)(pe[i] * (dp[mt][r0 + i] + Dq));
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int rr = 16 * kk + trow;
@@ -537,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
 
   if (qi < N) {
     uint16_t* dqr = p.dq + head + (size_t)qi * D;
-    const float sc = p.scale;
+    const float sc = p.scale * (DROP ? p.drop.scale : 1.0f);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -551,27 +610,27 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
 
 // ------------------------------------------------------------------ launchers
 // stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
-template <int D, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) {
   if (stages & 1) {
     const size_t rows_pad = (size_t)BH * p.Npad;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
-                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad);
+                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
     const int n_kt1 = (p.N + BWD_KV_BN - 1) / BWD_KV_BN;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_kt1)), dim3(512), 0,
-                       st, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_kt1)), dim3(512),
+                       0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
     const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG>), dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st,
-                       p);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_qt2)), dim3(256), 0,
+                       st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -592,6 +651,19 @@ hipError_t launch_bwd(const BwdParams& p, int BH, int d, bool causal, bool spars
                       hipStream_t st) {
   return d == 64 ? launch_bwd_d<64>(p, BH, causal, sparse, debug, stages, st)
                  : launch_bwd_d<128>(p, BH, causal, sparse, debug, stages, st);
+}
+
+// Backward with dropout.
+template <int D>
+hipError_t launch_bwd_dropout_d(const BwdParams& p, int BH, bool causal, bool sparse, int stages, hipStream_t st) {
+  if (causal) return sparse ? launch_bwd_t<D, true, true, false, true>(p, BH, stages, st) : launch_bwd_t<D, true, false, false, true>(p, BH, stages, st);
+  return sparse ? launch_bwd_t<D, false, true, false, true>(p, BH, stages, st) : launch_bwd_t<D, false, false, false, true>(p, BH, stages, st);
+}
+
+hipError_t launch_bwd_dropout(const BwdParams& p, int BH, int d, bool causal, bool sparse, int stages,
+                              hipStream_t st) {
+  return d == 64 ? launch_bwd_dropout_d<64>(p, BH, causal, sparse, stages, st)
+                 : launch_bwd_dropout_d<128>(p, BH, causal, sparse, stages, st);
 }
 
 }  // namespace fa

@@ -169,4 +169,67 @@ struct TileDMA {
   }
 };
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): each round multiplies counter
+// words 0 and 2 by the round constants into 64-bit products and forms the
+// new counter (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key advances by
+// the Weyl constants between rounds. The key is wave-uniform, so its
+// schedule stays in scalar registers.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// 4 x 4 transpose across the four lanes of a quad (lane t = lane % 4 holds
+// a[0..3]); afterwards lane t holds a[s] = the old a[t] of lane s. Two
+// exchange stages with quad-permute DPP moves: lanes t and t^1 swap the
+// off-diagonal elements of their 2 x 2 blocks, then lanes t and t^2.
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ void quad_transpose4(uint32_t (&a)[4], int t) {
+  const bool odd = (t & 1) != 0, hi = (t & 2) != 0;
+  {
+    const uint32_t r0 = quad_swap1(odd ? a[0] : a[1]);
+    const uint32_t r1 = quad_swap1(odd ? a[2] : a[3]);
+    if (odd) {
+      a[0] = r0;
+      a[2] = r1;
+    } else {
+      a[1] = r0;
+      a[3] = r1;
+    }
+  }
+  {
+    const uint32_t r0 = quad_swap2(hi ? a[0] : a[2]);
+    const uint32_t r1 = quad_swap2(hi ? a[1] : a[3]);
+    if (hi) {
+      a[0] = r0;
+      a[1] = r1;
+    } else {
+      a[2] = r0;
+      a[3] = r1;
+    }
+  }
+}
+
 }  // namespace fa

@@ -37,7 +37,7 @@
 
 namespace fa {
 
-template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 // Two 4-wave workgroups per CU unless the two K/V stages of one exceed half the LDS.
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = 32 * WAVES;  // query rows per workgroup
@@ -187,6 +187,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 #pragma unroll
       for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(t[r0 + i], c, -m_use));
       l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      if (DROP) {
+        // Dropout after the row sum (the softmax is of the undropped row):
+        // slots 0-3 are keys kd .. kd+3 and slots 4-7 keys kd+8 .. kd+11,
+        // each four consecutive keys one generator call.
+        const int kd = j * BN + 16 * kk + 4 * h2;
+        uint32_t w0[4], w1[4];
+        philox4x32_10((uint32_t)kd >> 2, (uint32_t)qi, (uint32_t)bh, p.drop.off, p.drop.k0, p.drop.k1, w0);
+        philox4x32_10((uint32_t)(kd + 8) >> 2, (uint32_t)qi, (uint32_t)bh, p.drop.off, p.drop.k0, p.drop.k1, w1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (w0[i] < p.drop.t) e[i] = 0.f;
+          if (w1[i] < p.drop.t) e[4 + i] = 0.f;
+        }
+      }
       const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(vT[dt], pb, oacc[dt]);
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 
   // Epilogue: O = acc / l (deferred normalisation), lse = ln sum exp.
   const float l_tot = xhalf_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.0f) / l_tot : 0.f;
   if (qi < N) {
     uint16_t* orow = p.o + head + (size_t)qi * D;
 #pragma unroll
@@ -246,10 +260,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   }
 }
 
-template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG>
+template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 hipError_t launch_fwd_t(const FwdParams& p, int BH, hipStream_t st) {
   const dim3 grid((unsigned)(BH * p.n_qt));
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BN, WAVES, CAUSAL, SPARSE, DEBUG>), grid, dim3(64 * WAVES), 0, st, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BN, WAVES, CAUSAL, SPARSE, DEBUG, DROP>), grid, dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 
@@ -292,6 +306,51 @@ hipError_t launch_fwd(const FwdParams& p, int BH, int d, int bm, int bn, bool ca
                       hipStream_t st) {
   return d == 64 ? launch_fwd_d<64>(p, BH, bm, bn, causal, sparse, debug, st)
                  : launch_fwd_d<128>(p, BH, bm, bn, causal, sparse, debug, st);
+}
+
+// Forward with dropout (default tiles only).
+template <int D>
+hipError_t launch_fwd_dropout_d(const FwdParams& p, int BH, bool causal, bool sparse, hipStream_t st) {
+  constexpr int W = FWD_BM / 32;
+  if (causal)
+    return sparse ? launch_fwd_t<D, FWD_BN, W, true, true, false, true>(p, BH, st)
+                  : launch_fwd_t<D, FWD_BN, W, true, false, false, true>(p, BH, st);
+  return sparse ? launch_fwd_t<D, FWD_BN, W, false, true, false, true>(p, BH, st)
+                : launch_fwd_t<D, FWD_BN, W, false, false, false, true>(p, BH, st);
+}
+
+hipError_t launch_fwd_dropout(const FwdParams& p, int BH, int d, bool causal, bool sparse, hipStream_t st) {
+  return d == 64 ? launch_fwd_dropout_d<64>(p, BH, causal, sparse, st)
+                 : launch_fwd_dropout_d<128>(p, BH, causal, sparse, st);
+}
+
+// Keep mask of the dropout generator, one byte per (b*H + h, i, j): one
+// thread per four consecutive keys of a row. For tests of the generator
+// against an independent implementation.
+__global__ __launch_bounds__(256) void fa_dropout_keep_kernel(uint8_t* __restrict__ keep, int N, int ngrp,
+                                                              size_t total, Dropout dr) {
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;  // (bh, i, group)
+  if (gid >= total) return;
+  const int grp = (int)(gid % ngrp);
+  const size_t row = gid / ngrp;  // bh * N + i
+  const int i = (int)(row % N);
+  const uint32_t bh = (uint32_t)(row / N);
+  uint32_t w[4];
+  philox4x32_10((uint32_t)grp, (uint32_t)i, bh, dr.off, dr.k0, dr.k1, w);
+  uint8_t* out = keep + row * N;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * grp + e;
+    if (j < N) out[j] = w[e] >= dr.t ? 1 : 0;
+  }
+}
+
+hipError_t launch_dropout_keep(uint8_t* keep, int BH, int N, const Dropout& dr, hipStream_t st) {
+  const int ngrp = (N + 3) / 4;
+  const size_t total = (size_t)BH * N * ngrp;
+  hipLaunchKernelGGL(fa_dropout_keep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, keep, N, ngrp,
+                     total, dr);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -26,6 +26,17 @@ constexpr int BWD_PAD_ROWS = 128;
 // Block-sparse masks are given at this granularity.
 constexpr int MASK_BLOCK = 128;
 
+// Attention dropout on the probabilities (counter-based keep mask, see
+// philox4x32_10 in fa_device.h): element (b*H + h, i, j) is kept iff word
+// j % 4 of Philox4x32-10(counter (j / 4, i, b*H + h, off), key (k0, k1)) is
+// >= t; kept probabilities are scaled by `scale` = 1 / (1 - p).
+struct Dropout {
+  uint32_t t;       // floor(p * 2^32)
+  uint32_t k0, k1;  // seed, low and high 32 bits
+  uint32_t off;     // offset (counter word 3)
+  float scale;      // 1 / (1 - p)
+};
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -37,6 +48,7 @@ struct FwdParams {
   int H, N;
   int n_qt, n_kt, nb;
   float c;  // scale * log2(e)
+  Dropout drop;  // used by the dropout instantiations only
 };
 
 struct BwdParams {
@@ -59,6 +71,8 @@ struct BwdParams {
   int nb;
   float c;      // scale * log2(e)
   float scale;  // scale, applied to dQ and dK
+  float dfac;   // factor on -D in the workspace: 1, or 1 - p with dropout
+  Dropout drop;  // used by the dropout instantiations only
 };
 
 }  // namespace fa

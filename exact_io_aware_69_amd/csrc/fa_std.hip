@@ -23,7 +23,6 @@ namespace fa {
 
 // One wave per score row, four rows per workgroup; each lane handles 4
 // consecutive columns per 256-column chunk.
-constexpr int STD_MAX_N = 16384;
 
 __device__ __forceinline__ bool std_visible(int i, int j, int N, bool causal, const uint8_t* mrow) {
   return j < N && (!causal || j <= i) && (!mrow || mrow[j / MASK_BLOCK] != 0);

@@ -61,7 +61,8 @@ typedef enum fa_status {
     FA_ERR_WORKSPACE = -5,      /* backward workspace missing or too small */
     FA_ERR_MASK = -6,           /* block_mask NULL in a block-sparse call */
     FA_ERR_HIP = -7,            /* a HIP launch, runtime or rocBLAS call failed */
-    FA_ERR_ALIGN = -8           /* a pointer is not 16-byte aligned */
+    FA_ERR_ALIGN = -8,          /* a pointer is not 16-byte aligned */
+    FA_ERR_DROPOUT = -9         /* dropout probability not in [0, 1) */
 } fa_status;
 
 /* Forward. Writes o [B][H][N][d] (bf16) and lse [B][H][N] (fp32).
@@ -164,6 +165,39 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  int B, int H, int N, int d, int causal, float scale,
                  const uint8_t* block_mask,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention dropout (the "PagedAttention" page lists dropout among
+ * attention's O(N^2) elementwise operations and defines nothing more; the
+ * semantics below are this library's reading). Dropout acts on the
+ * normalised probabilities before they multiply V:
+ *   O = (P o Z) V / (1 - p),   lse unchanged (that of the undropped row),
+ * with Z_ij in {0, 1} regenerated inside the kernels from a counter-based
+ * generator, Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011), so no mask is stored:
+ *   word j % 4 of Philox4x32-10(counter (j / 4, i, b*H + h, offset),
+ *                                key (seed mod 2^32, seed / 2^32))
+ * keeps key j of query row i iff it is >= floor(p * 2^32).
+ * The backward is the gradient with Z held fixed (same seed and offset as
+ * the forward): dV = (P o Z)^T dO / (1 - p), dP = (dO V^T) o Z / (1 - p),
+ * D = rowsum(dO o O), dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * Arguments as fa_fwd / fa_bwd, with block_mask NULL for dense attention,
+ * plus dropout_p in [0, 1) (else FA_ERR_DROPOUT), seed and offset. Default
+ * tile configuration only. */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   const uint8_t* block_mask, float dropout_p, uint64_t seed,
+                   uint32_t offset, void* stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, int causal, float scale,
+                   const uint8_t* block_mask, float dropout_p, uint64_t seed,
+                   uint32_t offset, void* workspace, size_t workspace_bytes,
+                   void* stream);
+/* The keep mask Z of the same generator, one byte (0 or 1) per element into
+ * keep, a device buffer uint8 [B][H][N][N] owned by the caller (tests of
+ * the generator; O(N^2) memory). */
+int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed,
+                    uint32_t offset, uint8_t* keep, void* stream);
 
 /* Tile sizes the kernels use, so a caller can size the visit maps below.
  * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel.

@@ -189,3 +189,22 @@ def test_fa1_fwd_argument_errors():
     assert _lib.fa_fwd_fa1(**{**args, "d": 80}) == -3
     assert _lib.fa_fwd_fa1(**{**args, "scale": 0.0}) == -4
     assert _lib.fa_fwd_fa1(**{**args, "workspace": FAKE + 4}) == -8
+
+
+def test_dropout_argument_errors():
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=64, d=64, causal=0, scale=0.125,
+                block_mask=None, dropout_p=0.1, seed=1, offset=0, stream=None)
+    for bad in (-0.1, 1.0, 1.5, float("nan")):
+        assert _lib.fa_fwd_dropout(**{**args, "dropout_p": bad}) == -9
+    assert _lib.fa_fwd_dropout(**{**args, "q": None}) == -1
+    assert _lib.fa_fwd_dropout(**{**args, "d": 96}) == -3
+    st, need = _lib.fa_bwd_workspace_size(1, 2, 64, 64)
+    bargs = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2, N=64, d=64,
+                 causal=1, scale=0.125, block_mask=None, dropout_p=0.1, seed=1, offset=0, workspace=FAKE,
+                 workspace_bytes=need, stream=None)
+    assert _lib.fa_bwd_dropout(**{**bargs, "dropout_p": 1.0}) == -9
+    assert _lib.fa_bwd_dropout(**{**bargs, "workspace_bytes": need - 1}) == -5
+    assert _lib.fa_dropout_keep(1, 1, 8, 0.5, 1, 0, None, None) == -1
+    assert _lib.fa_dropout_keep(1, 1, 0, 0.5, 1, 0, FAKE, None) == -2
+    assert _lib.fa_dropout_keep(1, 1, 8, -1.0, 1, 0, FAKE, None) == -9
+    assert "dropout" in _lib.fa_status_str(-9)
