@@ -134,13 +134,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // lds + size * lane. These wrappers are plain (non-template) functions:
 // target builtins reached from template instantiations break the host
 // compilation pass of the kernels.
+// tile_bytes is the same for every lane of the wave; readfirstlane states
+// so, and keeps the compiler from wrapping the copy in a per-lane loop when
+// it cannot prove the value uniform.
 __device__ __forceinline__ void dma4(const void* base, uint32_t bytes, int lane_off, int tile_bytes,
                                      FA_LDS void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 4, lane_off, tile_bytes, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 4, lane_off,
+                                           __builtin_amdgcn_readfirstlane(tile_bytes), 0, 0);
 }
 __device__ __forceinline__ void dma16(const void* base, uint32_t bytes, int lane_off, int tile_bytes,
                                       FA_LDS void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 16, lane_off, tile_bytes, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), lds, 16, lane_off,
+                                           __builtin_amdgcn_readfirstlane(tile_bytes), 0, 0);
 }
 
 template <int D, int ROWS, int WAVES = 4>

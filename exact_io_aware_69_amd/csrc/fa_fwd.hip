@@ -45,6 +45,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   constexpr int TILEB = BN * D * 2;
   constexpr int NS = BN / 32;  // 32-key blocks per tile
   constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 domain)
+  // LDS reads issued ahead of their products (below); not in the 8-wave
+  // d = 128, 128-key configuration, which has no registers left for them.
+  constexpr bool AHEAD = !(D == 128 && BN == 128 && WAVES == 8);
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   // Two LDS stages for K and two for V, as four separate objects: the stage
   // of every access is a compile-time constant (the loop is unrolled by
@@ -125,6 +128,18 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 #pragma unroll
       for (int mt = 0; mt < NS; ++mt)
         s[mt] = mfma32(ld_lds16(ks, tile_off<D>(32 * mt + (lane & 31), 16 * kk + 8 * h2)), qf[kk], s[mt]);
+    // Issue order: the K reads of the first two k-steps, then each k-step's
+    // products followed by the reads two k-steps ahead.
+    if constexpr (AHEAD) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NS, 0);
+#pragma unroll
+      for (int kk = 0; kk < D / 16 - 2; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   float m_run = -INFINITY;  // reference max of S * c (log2 domain)
@@ -172,15 +187,30 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     // P^T as B operand: slot i of half h2 in k-step kk is key
     // 16*kk + 8*(i/4) + 4*h2 + i%4, i.e. value r = 8*(kk%2) + i of block kk/2.
-#pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      // V^T fragments of this k-step first, so the LDS latency is covered
-      // by the exponentials below.
-      bf16x8 vT[D / 32];
+    // V^T fragments are read one k-step ahead: the reads of k-step kk + 1
+    // are issued before k-step kk's exponentials and products, so their LDS
+    // latency is covered by a whole k-step of work.
+    auto read_vt = [&](int kk, bf16x8 (&vT)[D / 32]) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
         vT[dt] = join_tr(ld_lds_tr(vs, tile_off<D>(16 * kk + vrow, 32 * dt + vcol)),
                          ld_lds_tr(vs, tile_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol)));
+    };
+    bf16x8 vnext[D / 32];
+    if constexpr (AHEAD) {
+      read_vt(0, vnext);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      bf16x8 vT[D / 32];
+      if constexpr (AHEAD) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) vT[dt] = vnext[dt];
+        if (kk + 1 < BN / 16) read_vt(kk + 1, vnext);
+      } else {
+        read_vt(kk, vT);
+      }
       const f32x16& t = s[kk >> 1];
       const int r0 = 8 * (kk & 1);
       float e[8];
@@ -204,11 +234,11 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
       const bf16x8 pb = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = mfma32(vT[dt], pb, oacc[dt]);
-      // Order within the k-step: the 8 transposed reads, then the vector
-      // work, then the 4 products; and nothing moves across k-steps (hoisting
-      // every V read of the tile would exceed the register budget of two
-      // waves per SIMD).
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+      // Order within the k-step: the next k-step's transposed reads, then
+      // the vector work, then this k-step's products; nothing moves across
+      // k-steps (hoisting every V read of the tile would exceed the
+      // register budget of two waves per SIMD).
+      if (!AHEAD || kk + 1 < BN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
       __builtin_amdgcn_sched_barrier(0);
