@@ -136,6 +136,48 @@ def head_backward_dropout(Q, K, V, dO, causal, scale, Z, p, mask_h=None, mask_bl
     return {"O": O, "lse": lse, "D": D, "dQ": s * (dS @ K), "dK": s * (dS.T @ Q), "dV": dV}
 
 
+def head_grad_rows_dropout(Q, K, V, dO, causal, scale, p, bh, seed, offset, rows, mask_h=None, mask_block=128):
+    """O, lse, D and dQ of the selected query rows of head index bh with
+    dropout (row i of dQ needs only row i of P, Z and dP)."""
+    N = K.shape[0]
+    s = _scale64(scale)
+    keep_p = 1.0 - float(np.float64(np.float32(p)))
+    rows = np.asarray(rows, dtype=np.int64)
+    Z = dropout_keep_head(bh, rows, np.arange(N), p, seed, offset)
+    O, lse = head_forward_dropout(Q, K, V, causal, scale, Z, p, mask_h, mask_block, rows=rows)
+    keep = keep_matrix(rows, np.arange(N), causal, mask_h, mask_block)
+    P = _probs_from_lse((Q[rows] @ K.T) * s, keep, lse)
+    D = np.sum(dO[rows] * O, axis=1)
+    dP = np.where(Z, dO[rows] @ V.T, 0.0) / keep_p
+    dS = P * (dP - D[:, None])
+    return {"O": O, "lse": lse, "D": D, "dQ": s * (dS @ K)}
+
+
+def head_grad_cols_dropout(Q, K, V, dO, causal, scale, p, bh, seed, offset, cols, mask_h=None, mask_block=128,
+                           row_chunk=1024):
+    """dK, dV of the selected key columns of head index bh with dropout;
+    lse and D of every row are recomputed row chunk by row chunk."""
+    N = Q.shape[0]
+    s = _scale64(scale)
+    keep_p = 1.0 - float(np.float64(np.float32(p)))
+    cols = np.asarray(cols, dtype=np.int64)
+    lse = np.empty(N)
+    D = np.empty(N)
+    for r0 in range(0, N, row_chunk):
+        rr = np.arange(r0, min(N, r0 + row_chunk))
+        Zr = dropout_keep_head(bh, rr, np.arange(N), p, seed, offset)
+        O_r, lse_r = head_forward_dropout(Q, K, V, causal, scale, Zr, p, mask_h, mask_block, rows=rr)
+        lse[rr] = lse_r
+        D[rr] = np.sum(dO[rr] * O_r, axis=1)
+    Z = dropout_keep_head(bh, np.arange(N), cols, p, seed, offset)
+    keep = keep_matrix(np.arange(N), cols, causal, mask_h, mask_block)
+    P = _probs_from_lse((Q @ K[cols].T) * s, keep, lse)
+    dV = (np.where(Z, P, 0.0) / keep_p).T @ dO
+    dP = np.where(Z, dO @ V[cols].T, 0.0) / keep_p
+    dS = P * (dP - D[:, None])
+    return {"dK": s * (dS.T @ Q), "dV": dV, "lse": lse, "D": D}
+
+
 def attn_fwd_dropout_ref(q, k, v, causal, scale, p, seed, offset, block_mask=None, mask_block=128):
     """Dropout forward over [B, H, N, d] bf16 bits: (O, lse) float64."""
     q, k, v = widen_bf16(q), widen_bf16(k), widen_bf16(v)

@@ -167,3 +167,23 @@ def test_planted_missing_scale_is_caught():
         num[idx] = (loss(Vp) - loss(Vm)) / (2 * h)
     assert np.abs(num - g["dV"]).max() < 1e-7
     assert np.abs(num - mutant_dV).max() > 1e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_and_column_pieces_match_full_backward(causal):
+    """The sampled-row and sampled-column dropout evaluations equal the full
+    backward on the same inputs (rows of dQ and columns of dK, dV are
+    independent pieces of the same definition)."""
+    rng = np.random.default_rng(12)
+    N, d, p, scale, seed, off, bh = 70, 8, 0.3, 0.4, 99, 2, 5
+    Q, K, V, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    Z = od.dropout_keep_head(bh, np.arange(N), np.arange(N), p, seed, off)
+    full = od.head_backward_dropout(Q, K, V, dO, causal, scale, Z, p)
+    rows = np.array([0, 1, 31, 32, 63, 69])
+    r = od.head_grad_rows_dropout(Q, K, V, dO, causal, scale, p, bh, seed, off, rows)
+    for name in ("O", "lse", "D", "dQ"):
+        np.testing.assert_allclose(r[name], full[name][rows], rtol=1e-12, atol=1e-12)
+    cols = np.array([0, 3, 4, 64, 69])
+    c = od.head_grad_cols_dropout(Q, K, V, dO, causal, scale, p, bh, seed, off, cols, row_chunk=16)
+    for name in ("dK", "dV"):
+        np.testing.assert_allclose(c[name], full[name][cols], rtol=1e-12, atol=1e-12)
