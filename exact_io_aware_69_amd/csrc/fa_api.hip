@@ -274,7 +274,10 @@ int fa_tile_config(int pass, int d, int* bm, int* bn) {
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   switch (pass) {
     case 0: *bm = fa::FWD_BM; *bn = fa::FWD_BN; return FA_OK;
-    case 1: *bm = fa::BWD_KV_BM; *bn = fa::BWD_KV_BN; return FA_OK;
+    case 1:
+      *bm = d == 128 ? fa::bwd_kv_bm<128>() : fa::bwd_kv_bm<64>();
+      *bn = d == 128 ? fa::bwd_kv_bn<128>() : fa::bwd_kv_bn<64>();
+      return FA_OK;
     case 2: *bm = fa::BWD_Q_BM; *bn = d == 128 ? fa::bwd_q_bn<128>() : fa::bwd_q_bn<64>(); return FA_OK;
     default: return FA_ERR_SHAPE;
   }

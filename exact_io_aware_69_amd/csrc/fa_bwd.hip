@@ -93,31 +93,35 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
 // transposed products), tile t (row products) and tile t+1 (being copied);
 // each stage also holds its tile's P.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
-__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int BNK = BWD_KV_BN;  // keys per workgroup
-  constexpr int BMQ = BWD_KV_BM;  // query rows per streamed tile
+__global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 : 2) void fa_bwd_dkdv_kernel(
+    const BwdParams p) {
+  constexpr int BNK = bwd_kv_bn<D>();  // keys per workgroup
+  constexpr int BMQ = bwd_kv_bm<D>();  // query rows per streamed tile
   constexpr int QB = BMQ / 32;    // 32-query blocks per tile
+  constexpr int KG = BNK / 32;    // key groups (one P-wave and one dS-wave each)
   constexpr int TILEB = BMQ * D * 2;
-  constexpr int PXB = 4 * QB * 2048;  // P of a tile: [key group][query block][half][lane] x 16 bytes
-  static_assert(BNK == MASK_BLOCK, "one key tile per mask column");
-  static_assert(BMQ == 64, "lse/D rows are copied by one wave-wide 4-byte copy");
+  constexpr int PXB = KG * QB * 2048;  // P of a tile: [key group][query block][half][lane] x 16 bytes
+  constexpr int LROW = 64;             // lse / -D floats per stage and array (one 4-byte copy per lane)
+  static_assert(2 * KG == bwd_kv_waves<D>() && KG >= 2, "one P-wave and one dS-wave per key group");
+  static_assert(MASK_BLOCK % BNK == 0 && MASK_BLOCK % BMQ == 0, "tiles lie inside one mask block");
+  static_assert(BMQ % 32 == 0 && BMQ <= LROW, "lse/D rows of a tile fit one wave-wide 4-byte copy");
   // Three stages of each kind of data, one array per kind.
   __shared__ __attribute__((aligned(1024))) uint8_t q_raw[3 * TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t o_raw[3 * TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t p_raw[3 * PXB];
-  __shared__ __attribute__((aligned(256))) float l_raw[3 * 2 * BMQ];  // per stage: lse*log2e rows, then -D rows
+  __shared__ __attribute__((aligned(256))) float l_raw[3 * 2 * LROW];  // per stage: lse*log2e rows, then -D rows
   struct Stage {
     FA_LDS uint8_t* q;   // Q tile
     FA_LDS uint8_t* o;   // dO tile
-    FA_LDS float* l;     // lse*log2e rows; -D rows at l + BMQ
+    FA_LDS float* l;     // lse*log2e rows; -D rows at l + LROW
     FA_LDS uint8_t* px;  // P of the tile
   };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h2 = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform (scalar)
-  const bool dswave = w >= 4;  // wave-uniform role
-  const int kg = w & 3;        // key group shared by waves kg and kg + 4
+  const bool dswave = w >= KG;         // wave-uniform role
+  const int kg = dswave ? w - KG : w;  // key group shared by waves kg and kg + KG
   const int n_kt = (p.N + BNK - 1) / BNK;
   const int n_qt = (p.N + BMQ - 1) / BMQ;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   const int it_begin = CAUSAL ? kb / BMQ : 0;
-  const uint8_t* mcol = SPARSE ? p.mask + (size_t)h * p.nb * p.nb + jt : nullptr;
+  const uint8_t* mcol = SPARSE ? p.mask + (size_t)h * p.nb * p.nb + (jt * BNK) / MASK_BLOCK : nullptr;
   auto next_tile = [&](int i) __attribute__((always_inline)) {
     if (SPARSE)
       while (i < n_qt && mcol[(size_t)((i * BMQ) / MASK_BLOCK) * p.nb] == 0) ++i;
@@ -162,12 +166,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   const float* Dg = p.Dneg + (size_t)bh * p.Npad;
   // The P-waves issue every tile copy: they wait at the barrier for their
   // partners anyway, so the dS-waves never stall on the copy queue.
-  const TileDMA<D, BMQ, 4> cp(kg, lane);
+  const TileDMA<D, BMQ, KG> cp(kg, lane);
   auto dma_q = [&](int i, const Stage& sb) __attribute__((always_inline)) {  // P-waves only
     cp.copy(p.q + head, head_bytes, i * BMQ * D * 2, sb.q, kg);
     cp.copy(p.dO + head, head_bytes, i * BMQ * D * 2, sb.o, kg);
     if (w == 0) dma4(l2g, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)sb.l);
-    if (w == 1) dma4(Dg, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)(sb.l + BMQ));
+    if (w == 1) dma4(Dg, row_bytes, lane * 4, i * BMQ * 4, (FA_LDS void*)(sb.l + LROW));
   };
 
   const float c = p.c;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (DSW) {
-        const FA_LDS float* dl = sb.l + BMQ;
+        const FA_LDS float* dl = sb.l + LROW;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
       if (DROP) {
         // Kept (P >= 0): dS = P (dP - D) with dP, D both in units of
         // 1 - p; dropped (P stored negated): dS = -P D = P' * D.
-        const FA_LDS float* dl = sb.l + BMQ;
+        const FA_LDS float* dl = sb.l + LROW;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_kernel(const BwdParams p) 
   auto needs_mask = [&](int i) __attribute__((always_inline)) { return CAUSAL && k0w + 31 > i * BMQ; };
   auto stage = [&](int S) __attribute__((always_inline)) {
     return Stage{(FA_LDS uint8_t*)q_raw + S * TILEB, (FA_LDS uint8_t*)o_raw + S * TILEB,
-                 (FA_LDS float*)l_raw + S * 2 * BMQ, (FA_LDS uint8_t*)p_raw + S * PXB};
+                 (FA_LDS float*)l_raw + S * 2 * LROW, (FA_LDS uint8_t*)p_raw + S * PXB};
   };
 
   // The whole sweep, instantiated once per role so that each role's
@@ -621,8 +625,9 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int n_kt1 = (p.N + BWD_KV_BN - 1) / BWD_KV_BN;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_kt1)), dim3(512),
+    const int n_kt1 = (p.N + bwd_kv_bn<D>() - 1) / bwd_kv_bn<D>();
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_kt1)),
+                       dim3(64 * bwd_kv_waves<D>()),
                        0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

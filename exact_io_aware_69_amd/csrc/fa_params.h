@@ -10,11 +10,18 @@ namespace fa {
 // the query rows of the tile, never the keys), key/value tiles of FWD_BN rows.
 constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
-// Backward dK/dV kernel: a workgroup of 8 waves owns BWD_KV_BN keys; waves
-// w and w + 4 share keys 32w .. 32w + 31 (one computes P and dV, the other
-// dP, dS and dK). Query tiles of BWD_KV_BM rows stream through LDS.
-constexpr int BWD_KV_BN = 128;
-constexpr int BWD_KV_BM = 64;
+// Backward dK/dV kernel: a workgroup owns bwd_kv_bn<D>() keys, one P-wave
+// and one dS-wave per 32 keys (one computes P and dV, the other dP, dS and
+// dK); query tiles of bwd_kv_bm<D>() rows stream through LDS. d = 128: 128
+// keys, 8 waves, 64-row tiles, one workgroup per CU. d = 64: 64 keys,
+// 4 waves, 32-row tiles, up to four workgroups per CU (measured faster at
+// d = 64, slower at d = 128 where only two fit).
+template <int D>
+constexpr int bwd_kv_bn() { return D == 128 ? 128 : 64; }
+template <int D>
+constexpr int bwd_kv_bm() { return D == 128 ? 64 : 32; }
+template <int D>
+constexpr int bwd_kv_waves() { return 2 * bwd_kv_bn<D>() / 32; }
 // Backward dQ kernel: a workgroup owns BWD_Q_BM queries (32 per wave) and
 // streams key tiles of bwd_q_bn<D>() rows (32 at d = 128 keeps a wave within
 // the 256 registers that two waves per SIMD allow).
