@@ -125,8 +125,14 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   const int n_kt = (p.N + BNK - 1) / BNK;
   const int n_qt = (p.N + BMQ - 1) / BMQ;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bh = lid / n_kt;
-  const int jt = lid % n_kt;  // ascending: for causal the first key tiles see the most queries
+  // Ascending key tiles: under causal the first ones see the most queries.
+  int bh, jt;
+  if (CAUSAL && !SPARSE) {
+    head_rank_order(lid, gridDim.x / n_kt, n_kt, bh, jt);
+  } else {
+    bh = lid / n_kt;
+    jt = lid % n_kt;
+  }
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -455,9 +461,15 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   const int n_qt = (p.N + BM - 1) / BM;
   const int n_kt = (p.N + BN - 1) / BN;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bh = lid / n_qt;
-  int qt = lid % n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest query tiles first
+  int bh, qt;
+  if (CAUSAL && !SPARSE) {  // longest query tiles first, across the XCD's heads
+    head_rank_order(lid, gridDim.x / n_qt, n_qt, bh, qt);
+    qt = n_qt - 1 - qt;
+  } else {
+    bh = lid / n_qt;
+    qt = lid % n_qt;
+    if (CAUSAL) qt = n_qt - 1 - qt;
+  }
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;

@@ -65,9 +65,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, wave-uniform (scalar)
 
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bh = lid / p.n_qt;
-  int qt = lid % p.n_qt;
-  if (CAUSAL) qt = p.n_qt - 1 - qt;  // longest query tiles first
+  int bh, qt;
+  if (CAUSAL && !SPARSE) {  // longest query tiles first, across the XCD's heads
+    head_rank_order(lid, gridDim.x / p.n_qt, p.n_qt, bh, qt);
+    qt = p.n_qt - 1 - qt;
+  } else {
+    bh = lid / p.n_qt;
+    qt = lid % p.n_qt;
+    if (CAUSAL) qt = p.n_qt - 1 - qt;
+  }
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
