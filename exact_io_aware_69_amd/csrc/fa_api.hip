@@ -91,6 +91,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.nb = (N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
   p.c = scale * 1.4426950408889634f;
   p.drop = drop ? *drop : fa::Dropout{0, 0, 0, 0, 1.0f};
+  p.hgrp = 1;  // set per launch
   hipError_t e = drop ? fa::launch_fwd_dropout(p, B * H, d, causal != 0, sparse, (hipStream_t)stream)
                       : fa::launch_fwd(p, B * H, d, bm, bn, causal != 0, sparse, visited != nullptr,
                                        (hipStream_t)stream);
@@ -133,6 +134,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.scale = scale;
   p.dfac = drop ? (float)(1.0 - (double)dropout_p) : 1.0f;
   p.drop = drop ? *drop : fa::Dropout{0, 0, 0, 0, 1.0f};
+  p.hgrp = 1;  // set per launch
   hipError_t e = drop ? fa::launch_bwd_dropout(p, B * H, d, causal != 0, sparse, stages, (hipStream_t)stream)
                       : fa::launch_bwd(p, B * H, d, causal != 0, sparse, visited_kv != nullptr, stages,
                                        (hipStream_t)stream);

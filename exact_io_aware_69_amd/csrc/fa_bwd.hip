@@ -127,12 +127,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   // Ascending key tiles: under causal the first ones see the most queries.
   int bh, jt;
-  if (CAUSAL && !SPARSE) {
-    head_rank_order(lid, gridDim.x / n_kt, n_kt, bh, jt);
-  } else {
-    bh = lid / n_kt;
-    jt = lid % n_kt;
-  }
+  head_rank_order(lid, n_kt, p.hgrp, bh, jt);
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -462,14 +457,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   const int n_kt = (p.N + BN - 1) / BN;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   int bh, qt;
-  if (CAUSAL && !SPARSE) {  // longest query tiles first, across the XCD's heads
-    head_rank_order(lid, gridDim.x / n_qt, n_qt, bh, qt);
-    qt = n_qt - 1 - qt;
-  } else {
-    bh = lid / n_qt;
-    qt = lid % n_qt;
-    if (CAUSAL) qt = n_qt - 1 - qt;
-  }
+  head_rank_order(lid, n_qt, p.hgrp, bh, qt);
+  if (CAUSAL) qt = n_qt - 1 - qt;  // longest query tiles first
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -636,18 +625,26 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // Dense causal launches interleave heads (see head_group); block-sparse
+  // work per tile depends on the mask, so those keep head order.
+  constexpr bool INTERLEAVE = CAUSAL && !SPARSE;
   if (stages & 2) {
     const int n_kt1 = (p.N + bwd_kv_bn<D>() - 1) / bwd_kv_bn<D>();
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_kt1)),
-                       dim3(64 * bwd_kv_waves<D>()),
-                       0, st, p);
+    const auto kernel = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
+    static const int wgs = wgs_per_cu((const void*)kernel, 64 * bwd_kv_waves<D>());
+    BwdParams q = p;
+    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, n_kt1) : 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * n_kt1)), dim3(64 * bwd_kv_waves<D>()), 0, st, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
     const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>), dim3((unsigned)(BH * n_qt2)), dim3(256), 0,
-                       st, p);
+    const auto kernel = fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
+    static const int wgs = wgs_per_cu((const void*)kernel, 256);
+    BwdParams q = p;
+    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, n_qt2) : 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

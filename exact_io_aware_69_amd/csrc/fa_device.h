@@ -99,16 +99,15 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-// (head, tile rank) of logical workgroup `lid` in a grid of BH heads x
-// `ntile` tiles whose per-head work falls with the rank (causal attention).
-// Each XCD receives a contiguous range of logical indices, one group of
-// G = BH / 8 heads when 8 divides BH. Within a group the order is rank-major:
-// rank 0 of every head, then rank 1, and so on, so the heaviest tiles of all
-// the XCD's heads are dispatched first. Ordering head by head instead starts
-// the last head's heavy tiles near the end of the launch and leaves the
-// XCD's other CUs idle while they finish.
-__device__ __forceinline__ void head_rank_order(int lid, int BH, int ntile, int& bh, int& rank) {
-  const int G = (BH % 8 == 0) ? BH / 8 : 1;
+// (head, tile rank) of logical workgroup `lid` in a grid of heads x
+// `ntile` tiles, ordered in groups of G consecutive heads (G divides the
+// number of heads): within a group, rank 0 of every head, then rank 1, and
+// so on. G = 1 is plain head-by-head order. For causal attention the rank
+// is ordered heaviest first; each XCD receives a contiguous range of
+// logical indices (xcd_grouped_block), so with G > 1 the heaviest tiles of
+// G heads start together instead of the last head's starting near the end
+// of the launch (the launcher picks G, see head_group).
+__device__ __forceinline__ void head_rank_order(int lid, int ntile, int G, int& bh, int& rank) {
   const int per = G * ntile;
   const int r = lid % per;
   rank = r / G;

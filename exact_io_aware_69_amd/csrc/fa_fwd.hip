@@ -66,14 +66,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   int bh, qt;
-  if (CAUSAL && !SPARSE) {  // longest query tiles first, across the XCD's heads
-    head_rank_order(lid, gridDim.x / p.n_qt, p.n_qt, bh, qt);
-    qt = p.n_qt - 1 - qt;
-  } else {
-    bh = lid / p.n_qt;
-    qt = lid % p.n_qt;
-    if (CAUSAL) qt = p.n_qt - 1 - qt;
-  }
+  head_rank_order(lid, p.n_qt, p.hgrp, bh, qt);
+  if (CAUSAL) qt = p.n_qt - 1 - qt;  // longest query tiles first
   const int h = bh % p.H;
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
@@ -298,8 +292,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 
 template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 hipError_t launch_fwd_t(const FwdParams& p, int BH, hipStream_t st) {
-  const dim3 grid((unsigned)(BH * p.n_qt));
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BN, WAVES, CAUSAL, SPARSE, DEBUG, DROP>), grid, dim3(64 * WAVES), 0, st, p);
+  const auto kernel = fa_fwd_kernel<D, BN, WAVES, CAUSAL, SPARSE, DEBUG, DROP>;
+  static const int wgs = wgs_per_cu((const void*)kernel, 64 * WAVES);
+  FwdParams q = p;
+  // Dense causal launches interleave heads (see head_group); block-sparse
+  // work per tile depends on the mask, so those keep head order.
+  q.hgrp = (CAUSAL && !SPARSE) ? head_group(wgs, cus_per_xcd(), BH, p.n_qt) : 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * p.n_qt)), dim3(64 * WAVES), 0, st, q);
   return hipGetLastError();
 }
 

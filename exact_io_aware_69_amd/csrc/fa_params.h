@@ -2,6 +2,7 @@
 // gfx950 kernels.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fa {
@@ -56,6 +57,7 @@ struct FwdParams {
   int n_qt, n_kt, nb;
   float c;  // scale * log2(e)
   Dropout drop;  // used by the dropout instantiations only
+  int hgrp;      // heads per dispatch group (head_rank_order), set by the launcher
 };
 
 struct BwdParams {
@@ -80,6 +82,48 @@ struct BwdParams {
   float scale;  // scale, applied to dQ and dK
   float dfac;   // factor on -D in the workspace: 1, or 1 - p with dropout
   Dropout drop;  // used by the dropout instantiations only
+  int hgrp;      // heads per dispatch group (head_rank_order), set per launch
 };
+
+// Workgroups of `kernel` (launched with `block` threads, no dynamic LDS)
+// that one CU holds at once; 1 if the runtime cannot tell (the error is
+// cleared so that the launch that follows reports only its own).
+inline int wgs_per_cu(const void* kernel, int block) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  return n;
+}
+// CUs of one XCD of the current device (eight XCDs per device).
+inline int cus_per_xcd() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) {
+    (void)hipGetLastError();
+    return 32;
+  }
+  return cus / 8;
+}
+
+// Heads per dispatch group for a launch of BH heads x ntile tiles whose
+// per-head work falls with the tile rank (causal), given the workgroups one
+// CU holds and the CUs of one XCD. Each XCD runs BH / 8 consecutive heads.
+// Ordered head by head, the last head's heavy tiles start near the end and
+// the XCD idles while they finish; interleaving G heads rank by rank starts
+// the heavy tiles of G heads together. Too large a G spreads the XCD's
+// slots over more heads at once and lowers the L2 reuse of each head's K/V
+// (or Q/dO). G is the smallest divisor of BH / 8 with G * ntile >= 2 *
+// slots (1 when 8 does not divide BH): measured on causal d = 64 and 128
+// shapes, it was as fast as or faster than both G = 1 and G = BH / 8.
+inline int head_group(int wgs_per_cu, int cus_per_xcd, int BH, int ntile) {
+  if (BH % 8 != 0 || ntile < 1) return 1;
+  const int hx = BH / 8;
+  const int slots = wgs_per_cu * cus_per_xcd;
+  int g = 1;
+  while (g < hx && (g * ntile < 2 * slots || hx % g != 0)) ++g;
+  return g;
+}
 
 }  // namespace fa
