@@ -99,21 +99,6 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-// (head, tile rank) of logical workgroup `lid` in a grid of heads x
-// `ntile` tiles, ordered in groups of G consecutive heads (G divides the
-// number of heads): within a group, rank 0 of every head, then rank 1, and
-// so on. G = 1 is plain head-by-head order. For causal attention the rank
-// is ordered heaviest first; each XCD receives a contiguous range of
-// logical indices (xcd_grouped_block), so with G > 1 the heaviest tiles of
-// G heads start together instead of the last head's starting near the end
-// of the launch (the launcher picks G, see head_group).
-__device__ __forceinline__ void head_rank_order(int lid, int ntile, int G, int& bh, int& rank) {
-  const int per = G * ntile;
-  const int r = lid % per;
-  rank = r / G;
-  bh = (lid / per) * G + r % G;
-}
-
 // Wait until this wave's outstanding memory loads (including copies into LDS)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)

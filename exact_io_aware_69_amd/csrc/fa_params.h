@@ -85,6 +85,21 @@ struct BwdParams {
   int hgrp;      // heads per dispatch group (head_rank_order), set per launch
 };
 
+// (head, tile rank) of logical workgroup `lid` in a grid of heads x
+// `ntile` tiles, ordered in groups of G consecutive heads (G divides the
+// number of heads): within a group, rank 0 of every head, then rank 1, and
+// so on. G = 1 is plain head-by-head order. For causal attention the rank
+// is ordered heaviest first; each XCD receives a contiguous range of
+// logical indices (xcd_grouped_block), so with G > 1 the heaviest tiles of
+// G heads start together instead of the last head's starting near the end
+// of the launch (the launcher picks G, see head_group).
+__host__ __device__ inline void head_rank_order(int lid, int ntile, int G, int& bh, int& rank) {
+  const int per = G * ntile;
+  const int r = lid % per;
+  rank = r / G;
+  bh = (lid / per) * G + r % G;
+}
+
 // Workgroups of `kernel` (launched with `block` threads, no dynamic LDS)
 // that one CU holds at once; 1 if the runtime cannot tell (the error is
 // cleared so that the launch that follows reports only its own).
