@@ -38,7 +38,7 @@ SIGNATURES = {
     "fa_bwd_dropout": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _f, _u64, _u32, _p, _sz,
                             _p]),
     "fa_dropout_keep": (_i, [_i, _i, _i, _f, _u64, _u32, _p, _p]),
-    "fa_tile_config": (_i, [_i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "fa_tile_config": (_i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "fa_fwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p]),
     "fa_bwd_debug_visits": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz,
                                  _p, _p, _p]),
@@ -156,10 +156,10 @@ def fa_dropout_keep(B, H, N, dropout_p, seed, offset, keep, stream):
     return lib().fa_dropout_keep(B, H, N, dropout_p, seed, offset, keep, stream)
 
 
-def fa_tile_config(pass_, d):
+def fa_tile_config(pass_, d, causal):
     """Returns (status, bm, bn)."""
     bm, bn = _i(0), _i(0)
-    st = lib().fa_tile_config(pass_, d, ctypes.byref(bm), ctypes.byref(bn))
+    st = lib().fa_tile_config(pass_, d, int(causal), ctypes.byref(bm), ctypes.byref(bn))
     return st, bm.value, bn.value
 
 

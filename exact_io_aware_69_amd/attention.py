@@ -71,8 +71,8 @@ def backward(q, k, v, o, lse, dO, causal: bool = False, scale: float | None = No
     return dq, dk, dv
 
 
-def tile_config(pass_: int, d: int):
-    st, bm, bn = _lib.fa_tile_config(pass_, d)
+def tile_config(pass_: int, d: int, causal: bool):
+    st, bm, bn = _lib.fa_tile_config(pass_, d, causal)
     _lib.check(st, "fa_tile_config")
     return bm, bn
 
@@ -82,7 +82,7 @@ def forward_visits(q, k, v, causal, scale=None, block_mask=None):
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    bm, bn = tile_config(0, d)
+    bm, bn = tile_config(0, d, causal)
     vis = torch.zeros((B, H, -(-N // bm), -(-N // bn)), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -98,8 +98,8 @@ def backward_visits(q, k, v, o, lse, dO, causal, scale=None, block_mask=None):
     _check_inputs(q, k, v, o, dO)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    bm1, bn1 = tile_config(1, d)
-    bm2, bn2 = tile_config(2, d)
+    bm1, bn1 = tile_config(1, d, causal)
+    bm2, bn2 = tile_config(2, d, causal)
     vkv = torch.zeros((B, H, -(-N // bn1), -(-N // bm1)), dtype=torch.uint8, device=q.device)
     vq = torch.zeros((B, H, -(-N // bm2), -(-N // bn2)), dtype=torch.uint8, device=q.device)
     nbytes = workspace_bytes(B, H, N, d)

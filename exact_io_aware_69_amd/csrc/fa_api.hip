@@ -271,7 +271,7 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed, uint32_
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_tile_config(int pass, int d, int* bm, int* bn) {
+int fa_tile_config(int pass, int d, int causal, int* bm, int* bn) {
   if (!bm || !bn) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   switch (pass) {
@@ -280,7 +280,13 @@ int fa_tile_config(int pass, int d, int* bm, int* bn) {
       *bm = d == 128 ? fa::bwd_kv_bm<128>() : fa::bwd_kv_bm<64>();
       *bn = d == 128 ? fa::bwd_kv_bn<128>() : fa::bwd_kv_bn<64>();
       return FA_OK;
-    case 2: *bm = fa::BWD_Q_BM; *bn = d == 128 ? fa::bwd_q_bn<128>() : fa::bwd_q_bn<64>(); return FA_OK;
+    case 2:
+      *bm = fa::BWD_Q_BM;
+      if (d == 64)
+        *bn = fa::bwd_q_bn<64, false, false>();
+      else
+        *bn = causal ? fa::bwd_q_bn<128, true, false>() : fa::bwd_q_bn<128, false, false>();
+      return FA_OK;
     default: return FA_ERR_SHAPE;
   }
 }

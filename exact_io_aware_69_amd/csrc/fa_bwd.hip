@@ -440,7 +440,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = BWD_Q_BM;
-  constexpr int BN = bwd_q_bn<D>();
+  constexpr int BN = bwd_q_bn<D, CAUSAL, DROP>();
   constexpr int NS = BN / 32;
   constexpr int TILEB = BN * D * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t k0_raw[TILEB];

@@ -24,11 +24,13 @@ constexpr int bwd_kv_bm() { return D == 128 ? 64 : 32; }
 template <int D>
 constexpr int bwd_kv_waves() { return 2 * bwd_kv_bn<D>() / 32; }
 // Backward dQ kernel: a workgroup owns BWD_Q_BM queries (32 per wave) and
-// streams key tiles of bwd_q_bn<D>() rows (32 at d = 128 keeps a wave within
-// the 256 registers that two waves per SIMD allow).
+// streams key tiles of bwd_q_bn() rows. 64-key tiles halve the copies and
+// barriers per product; at d = 128 they fit the 256 registers that two
+// waves per SIMD allow only in the causal kernel without dropout (the others
+// spill), so those use 32-key tiles.
 constexpr int BWD_Q_BM = 128;
-template <int D>
-constexpr int bwd_q_bn() { return D == 128 ? 32 : 64; }
+template <int D, bool CAUSAL, bool DROP>
+constexpr int bwd_q_bn() { return (D == 64 || (CAUSAL && !DROP)) ? 64 : 32; }
 // Workspace rows per head are padded to a multiple of this.
 constexpr int BWD_PAD_ROWS = 128;
 // Block-sparse masks are given at this granularity.

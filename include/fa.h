@@ -200,9 +200,11 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed,
                     uint32_t offset, uint8_t* keep, void* stream);
 
 /* Tile sizes the kernels use, so a caller can size the visit maps below.
- * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel.
- * bm = query rows per tile, bn = key rows per tile. */
-int fa_tile_config(int pass, int d, int* bm, int* bn);
+ * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel;
+ * causal: nonzero for the causal kernels (the d = 128 dQ kernel streams
+ * 64-key tiles when causal, 32-key tiles otherwise). bm = query rows per
+ * tile, bn = key rows per tile. */
+int fa_tile_config(int pass, int d, int causal, int* bm, int* bn);
 
 /* Debug forward: same computation as fa_fwd_blocksparse (block_mask may be
  * NULL for dense) and additionally writes visited, uint8

@@ -46,13 +46,17 @@ def test_status_strings():
 
 def test_tile_config():
     for d in (64, 128):
-        for ps in (0, 1, 2):
-            st, bm, bn = _lib.fa_tile_config(ps, d)
-            assert st == 0 and bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
-            assert 128 % bm == 0 or bm % 128 == 0
-            assert 128 % bn == 0
-    assert _lib.fa_tile_config(0, 96)[0] == -3
-    assert _lib.fa_tile_config(7, 64)[0] == -2
+        for causal in (0, 1):
+            for ps in (0, 1, 2):
+                st, bm, bn = _lib.fa_tile_config(ps, d, causal)
+                assert st == 0 and bm > 0 and bn > 0 and bm % 32 == 0 and bn % 32 == 0
+                assert 128 % bm == 0 or bm % 128 == 0
+                assert 128 % bn == 0
+    # the d = 128 dQ kernel streams 64-key tiles only when causal
+    assert _lib.fa_tile_config(2, 128, 1)[2] == 64 and _lib.fa_tile_config(2, 128, 0)[2] == 32
+    assert _lib.fa_tile_config(2, 64, 0)[2] == _lib.fa_tile_config(2, 64, 1)[2] == 64
+    assert _lib.fa_tile_config(0, 96, 0)[0] == -3
+    assert _lib.fa_tile_config(7, 64, 0)[0] == -2
 
 
 def test_workspace_size_is_linear_in_N():

@@ -39,9 +39,9 @@ def test_visit_maps(case):
     o, lse, vis = attention.forward_visits(q, k, v, causal, scale, m)
     _, _, _, vkv, vq = attention.backward_visits(q, k, v, o, lse, do, causal, scale, m)
     torch.cuda.synchronize()
-    bm0, bn0 = attention.tile_config(0, d)
-    bm1, bn1 = attention.tile_config(1, d)
-    bm2, bn2 = attention.tile_config(2, d)
+    bm0, bn0 = attention.tile_config(0, d, causal)
+    bm1, bn1 = attention.tile_config(1, d, causal)
+    bm2, bn2 = attention.tile_config(2, d, causal)
     e0 = expected_visits(N, bm0, bn0, causal, mask, H)
     e1 = expected_visits(N, bm1, bn1, causal, mask, H, key_major=True)
     e2 = expected_visits(N, bm2, bn2, causal, mask, H)
