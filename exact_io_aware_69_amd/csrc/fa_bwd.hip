@@ -105,6 +105,13 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   static_assert(2 * KG == bwd_kv_waves<D>() && KG >= 2, "one P-wave and one dS-wave per key group");
   static_assert(MASK_BLOCK % BNK == 0 && MASK_BLOCK % BMQ == 0, "tiles lie inside one mask block");
   static_assert(BMQ % 32 == 0 && BMQ <= LROW, "lse/D rows of a tile fit one wave-wide 4-byte copy");
+  // P-waves accumulate dV^T by head-dimension block (block kg, all keys of
+  // the workgroup) rather than by key group: a 32-column block of dO^T is a
+  // quarter of the transposing LDS reads of the full d. Needs one block per
+  // key group, and P in LDS as the P-wave computed it (with dropout that copy
+  // carries the keep bit in its sign, so the dropout kernels keep the key
+  // split).
+  constexpr bool DV_BY_D = !DROP && D / 32 == KG;
   // Three stages of each kind of data, one array per kind.
   __shared__ __attribute__((aligned(1024))) uint8_t q_raw[3 * TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t o_raw[3 * TILEB];
@@ -240,6 +247,48 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   // 16*ks + 8*(e/4) + 4*hh + e%4 on both operands.
   auto products_b = [&](auto role, const Stage& sb) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!decltype(role)::value && DV_BY_D) {
+      // P-wave kg: dV^T rows of head-dimension block kg for all KG key
+      // groups, from the P that every P-wave stored for its partner. One
+      // transposed dO^T fragment (two transposing reads) feeds KG products,
+      // one per key group, whose P operand is a plain 16-byte row read.
+      const FA_LDS uint8_t* a2 = sb.o;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int rr = 32 * qb + 16 * ks + trow;
+          const int cc = 32 * kg + tcol;
+          const bf16x8 aT = join_tr(ld_lds_tr(a2, tile_off<D>(rr, cc)), ld_lds_tr(a2, tile_off<D>(rr + 8, cc)));
+#pragma unroll
+          for (int g2 = 0; g2 < KG; ++g2) {
+            const bf16x8 pb =
+                *reinterpret_cast<const FA_LDS bf16x8*>(sb.px + (g2 * QB + qb) * 2048 + ks * 1024 + lane * 16);
+            acc[g2] = mfma32(aT, pb, acc[g2]);
+          }
+        }
+      // Issue order: the reads of the first (query block, k-step) unit, then
+      // each unit's products, each followed by reads of the next unit.
+      constexpr int NU = QB * 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + KG, 0);
+#pragma unroll
+      for (int u = 0; u < NU - 1; ++u) {
+        // 2 + KG reads per unit: two after each of the first two products,
+        // one after each of the others.
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int g2 = 2; g2 < KG; ++g2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KG, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     const FA_LDS uint8_t* a2 = decltype(role)::value ? sb.q : sb.o;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -422,7 +471,22 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   else
     sweep(std::false_type());
 
-  if (key < N) {
+  if (DV_BY_D && !dswave) {
+    // dV of head-dimension block kg for the keys of every key group.
+#pragma unroll
+    for (int g2 = 0; g2 < KG; ++g2) {
+      const int key2 = kb + 32 * g2 + (lane & 31);
+      if (key2 < N) {
+        uint16_t* dst = p.dv + head + (size_t)key2 * D;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = 32 * kg + 8 * rg + 4 * h2;
+          *reinterpret_cast<u32x2*>(dst + d0) =
+              pack4_bf16(acc[g2][4 * rg], acc[g2][4 * rg + 1], acc[g2][4 * rg + 2], acc[g2][4 * rg + 3]);
+        }
+      }
+    }
+  } else if (key < N) {
     uint16_t* dst = (dswave ? p.dk : p.dv) + head + (size_t)key * D;
     const float sc = (dswave ? p.scale : 1.0f) * (DROP ? p.drop.scale : 1.0f);
 #pragma unroll
