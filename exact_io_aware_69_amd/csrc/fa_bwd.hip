@@ -36,6 +36,11 @@
 namespace fa {
 
 // ------------------------------------------------------------------ -D = -rowsum(dO o O), lse * log2(e)
+// Rows per thread of the preprocess: every thread issues the loads of all
+// its rows before using any, so enough bytes are in flight to stream O and dO
+// at close to the HBM rate.
+constexpr int PRE_ROWS = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dO,
@@ -43,33 +48,44 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
                                                          float* __restrict__ Dneg, float* __restrict__ lse2,
                                                          int N, int Npad, size_t rows_pad, float dfac) {
   constexpr int CH = D / 8;      // lanes per row, 8 elements each
-  constexpr int RPB = 256 / CH;  // rows per workgroup
-  const size_t prow = (size_t)blockIdx.x * RPB + threadIdx.x / CH;
+  constexpr int RPB = 256 / CH;  // rows per workgroup and pass
   const int c = threadIdx.x % CH;
-  const size_t bh = prow / Npad;
-  const int r = (int)(prow - bh * Npad);
-  const bool real = prow < rows_pad && r < N;
-  const size_t row = bh * N + r;
-  float acc = 0.f;
-  if (real) {
-    const u32x4 a = ld_global16(o + row * D + 8 * c);
-    const u32x4 b = ld_global16(dO + row * D + 8 * c);
+  size_t prow[PRE_ROWS], row[PRE_ROWS];
+  bool real[PRE_ROWS];
+  u32x4 a[PRE_ROWS], b[PRE_ROWS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
-      acc = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u), acc);
+  for (int i = 0; i < PRE_ROWS; ++i) {
+    prow[i] = (size_t)blockIdx.x * (RPB * PRE_ROWS) + (size_t)i * RPB + threadIdx.x / CH;
+    const size_t bh = prow[i] / Npad;
+    const int r = (int)(prow[i] - bh * Npad);
+    real[i] = prow[i] < rows_pad && r < N;
+    row[i] = bh * N + r;
+    a[i] = u32x4{0, 0, 0, 0};
+    b[i] = u32x4{0, 0, 0, 0};
+    if (real[i]) {
+      a[i] = ld_global16(o + row[i] * D + 8 * c);
+      b[i] = ld_global16(dO + row[i] * D + 8 * c);
     }
   }
 #pragma unroll
-  for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (prow < rows_pad && c == 0) {
-    float l2 = INFINITY;
-    if (real) {
-      const float l = lse[row];
-      l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+  for (int i = 0; i < PRE_ROWS; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(a[i][e] << 16), __uint_as_float(b[i][e] << 16), acc);
+      acc = fmaf(__uint_as_float(a[i][e] & 0xFFFF0000u), __uint_as_float(b[i][e] & 0xFFFF0000u), acc);
     }
-    Dneg[prow] = -acc * dfac;
-    lse2[prow] = l2;
+#pragma unroll
+    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (prow[i] < rows_pad && c == 0) {
+      float l2 = INFINITY;
+      if (real[i]) {
+        const float l = lse[row[i]];
+        l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      }
+      Dneg[prow[i]] = -acc * dfac;
+      lse2[prow[i]] = l2;
+    }
   }
 }
 
@@ -683,7 +699,7 @@ template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) {
   if (stages & 1) {
     const size_t rows_pad = (size_t)BH * p.Npad;
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (D / 8) * PRE_ROWS;  // rows per workgroup
     hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
                        p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac);
     const hipError_t e = hipGetLastError();
