@@ -658,7 +658,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
         const bf16x8 kT = join_tr(ld_lds_tr(ks, tile_off<D>(rr, cc)), ld_lds_tr(ks, tile_off<D>(rr + 8, cc)));
         dqt[dt] = mfma32(kT, dsb, dqt[dt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // No scheduling fence between k-steps: the next k-step's transposing
+      // reads may start during this one's vector work (0.4-1.9% faster than
+      // fencing each k-step, and no more registers).
     }
   };
 
