@@ -173,10 +173,14 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   const int it_begin = CAUSAL ? kb / BMQ : 0;
-  const uint8_t* mcol = SPARSE ? p.mask + (size_t)h * p.nb * p.nb + (jt * BNK) / MASK_BLOCK : nullptr;
+  MaskScan scan;  // kept blocks of the mask column of this key tile
+  if (SPARSE) scan.init(p.mask + (size_t)h * p.nb * p.nb + (jt * BNK) / MASK_BLOCK, nullptr, p.nb, p.nb);
   auto next_tile = [&](int i) __attribute__((always_inline)) {
-    if (SPARSE)
-      while (i < n_qt && mcol[(size_t)((i * BMQ) / MASK_BLOCK) * p.nb] == 0) ++i;
+    if (SPARSE && i < n_qt) {
+      const int b = (i * BMQ) / MASK_BLOCK;
+      const int bk = scan.next_kept(b);
+      if (bk != b) i = bk * (MASK_BLOCK / BMQ);
+    }
     return i;
   };
 
@@ -527,6 +531,7 @@ template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = BWD_Q_BM;
   constexpr int BN = bwd_q_bn<D, CAUSAL, DROP>();
+  static_assert(MASK_BLOCK % BN == 0 && MASK_BLOCK % BM == 0, "tiles lie inside one mask block");
   constexpr int NS = BN / 32;
   constexpr int TILEB = BN * D * 2;
   __shared__ __attribute__((aligned(1024))) uint8_t k0_raw[TILEB];
@@ -554,10 +559,14 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   const int qi = q0 + (lane & 31);
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(kt_end, q_last / BN + 1);
-  const uint8_t* mrow = SPARSE ? p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb : nullptr;
+  MaskScan scan;  // kept blocks of the mask row of this query tile
+  if (SPARSE) scan.init(p.mask + ((size_t)h * p.nb + (q_lo / MASK_BLOCK)) * p.nb, nullptr, 1, p.nb);
   auto next_tile = [&](int j) __attribute__((always_inline)) {
-    if (SPARSE)
-      while (j < kt_end && mrow[(j * BN) / MASK_BLOCK] == 0) ++j;
+    if (SPARSE && j < kt_end) {
+      const int b = (j * BN) / MASK_BLOCK;
+      const int bk = scan.next_kept(b);
+      if (bk != b) j = bk * (MASK_BLOCK / BN);
+    }
     return j;
   };
   auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BN <= q0 + 31; };

@@ -174,6 +174,59 @@ struct TileDMA {
   }
 };
 
+// Wave-wide ballot: bit l is lane l's predicate.
+__device__ __forceinline__ uint64_t ballot64(bool pred) { return __builtin_amdgcn_ballot_w64(pred); }
+
+// The kept blocks of one row of a block mask (or one column, with a stride),
+// read 64 blocks at a time: lane l loads the byte of block wb + l and a
+// ballot packs the window into one 64-bit word. The skip decisions of a tile
+// loop are then bit operations on that word, with one memory round trip per
+// 64 blocks instead of one per tile. row2, when not null, is a second row
+// whose kept blocks are added (a tile that spans two mask rows). Every lane
+// of the wave calls the members together, with wave-uniform arguments.
+struct MaskScan {
+  const uint8_t* row;
+  const uint8_t* row2;
+  int stride;     // bytes between consecutive blocks
+  int nb;         // blocks in the row
+  int wb;         // first block of the loaded window, -1 before the first load
+  uint64_t bits;  // bit k: block wb + k is kept
+
+  __device__ __forceinline__ void init(const uint8_t* r, const uint8_t* r2, int s, int n) {
+    row = r;
+    row2 = r2;
+    stride = s;
+    nb = n;
+    wb = -1;
+    bits = 0;
+  }
+  __device__ __forceinline__ void load(int b) {
+    wb = b & ~63;
+    const int i = wb + (int)(threadIdx.x & 63);
+    bool k = false;
+    if (i < nb) {
+      k = row[(size_t)i * stride] != 0;
+      if (row2) k = k || row2[(size_t)i * stride] != 0;
+    }
+    bits = ballot64(k);
+  }
+  // Whether block b (0 <= b < nb) is kept.
+  __device__ __forceinline__ bool kept(int b) {
+    if (wb < 0 || b < wb || b >= wb + 64) load(b);
+    return ((bits >> (b - wb)) & 1) != 0;
+  }
+  // First kept block >= b, or a value >= nb when there is none.
+  __device__ __forceinline__ int next_kept(int b) {
+    while (b < nb) {
+      if (wb < 0 || b < wb || b >= wb + 64) load(b);
+      const uint64_t m = bits >> (b - wb);
+      if (m != 0) return b + __builtin_ctzll(m);
+      b = wb + 64;
+    }
+    return b;
+  }
+};
+
 // Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
 // numbers: as easy as 1, 2, 3", SC 2011): each round multiplies counter
 // words 0 and 2 by the round constants into 64-bit products and forms the

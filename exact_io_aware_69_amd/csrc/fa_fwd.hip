@@ -41,7 +41,7 @@ template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool D
 // Two 4-wave workgroups per CU unless the two K/V stages of one exceed half the LDS.
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = 32 * WAVES;  // query rows per workgroup
-  static_assert(BN <= MASK_BLOCK && BM <= 2 * MASK_BLOCK, "a tile spans at most one mask column, two mask rows");
+  static_assert(MASK_BLOCK % BN == 0 && BM <= 2 * MASK_BLOCK, "a tile spans at most one mask column, two mask rows");
   constexpr int TILEB = BN * D * 2;
   constexpr int NS = BN / 32;  // 32-key blocks per tile
   constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 domain)
@@ -81,23 +81,26 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   // Block-sparse: the query tile spans one or two 128-row mask blocks. The
   // workgroup visits a key tile when any of them keeps it; a wave computes
   // it only when the block of its own 32 queries keeps it.
-  const uint8_t* mrow0 = nullptr;
-  const uint8_t* mrow1 = nullptr;
-  const uint8_t* mroww = nullptr;
+  MaskScan scan_wg, scan_w;  // kept blocks of the workgroup's mask rows, of this wave's row
   if (SPARSE) {
     const uint8_t* mh = p.mask + (size_t)h * p.nb * p.nb;
-    mrow0 = mh + (size_t)(q_lo / MASK_BLOCK) * p.nb;
-    mrow1 = mh + (size_t)(q_last / MASK_BLOCK) * p.nb;
-    mroww = mh + (size_t)(min(q0, N - 1) / MASK_BLOCK) * p.nb;
+    const uint8_t* mrow0 = mh + (size_t)(q_lo / MASK_BLOCK) * p.nb;
+    const uint8_t* mrow1 = mh + (size_t)(q_last / MASK_BLOCK) * p.nb;
+    scan_wg.init(mrow0, mrow1 != mrow0 ? mrow1 : nullptr, 1, p.nb);
+    scan_w.init(mh + (size_t)(min(q0, N - 1) / MASK_BLOCK) * p.nb, nullptr, 1, p.nb);
   }
   auto next_tile = [&](int j) __attribute__((always_inline)) {
-    if (SPARSE)
-      while (j < kt_end && mrow0[(j * BN) / MASK_BLOCK] == 0 && mrow1[(j * BN) / MASK_BLOCK] == 0) ++j;
+    if (SPARSE && j < kt_end) {
+      const int b = (j * BN) / MASK_BLOCK;
+      const int bk = scan_wg.next_kept(b);
+      if (bk != b) j = bk * (MASK_BLOCK / BN);
+    }
     return j;
   };
-  // Whether this wave computes tile j: some query of the wave sees some key.
+  // Whether this wave computes tile j (< kt_end): some query of the wave
+  // sees some key.
   auto wave_active = [&](int j) __attribute__((always_inline)) {
-    return (!CAUSAL || j * BN <= q0 + 31) && (!SPARSE || mroww[(j * BN) / MASK_BLOCK] != 0);
+    return (!CAUSAL || j * BN <= q0 + 31) && (!SPARSE || scan_w.kept((j * BN) / MASK_BLOCK));
   };
 
   // Q^T fragment (B operand): lane holds Q[qi][16*kk + 8*h2 .. +7].
@@ -247,17 +250,21 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 
   int jc = next_tile(0);
   if (jc < kt_end) {
+    bool act = wave_active(jc);
     dma_kv(jc, kst[0], vst[0]);
     wait_vmem();
     __syncthreads();
     // One step (parity P = index of the current tile mod 2): tile jc is in
-    // stage P; the next visited tile is copied into stage 1-P meanwhile.
+    // stage P; the next visited tile is copied into stage 1-P meanwhile. Its
+    // skip decisions are taken before that copy is issued, so a mask read
+    // never waits behind it.
     auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
       constexpr int P = decltype(parity)::value;
       const int jn = next_tile(jc + 1);
+      const bool act_n = jn < kt_end && wave_active(jn);
       if (jn < kt_end) dma_kv(jn, kst[1 - P], vst[1 - P]);
       if (DEBUG && tid == 0) p.visited[((size_t)bh * p.n_qt + qt) * p.n_kt + jc] = 1;
-      if (wave_active(jc)) {
+      if (act) {
         f32x16 s[NS];
         scores(kst[P], s);
         const bool need_mask = (jc * BN + BN > N) || (CAUSAL && jc * BN + BN - 1 > q0);
@@ -266,6 +273,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
       wait_vmem();
       __syncthreads();
       jc = jn;
+      act = act_n;
       return jn < kt_end;
     };
     while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
