@@ -45,9 +45,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   constexpr int TILEB = BN * D * 2;
   constexpr int NS = BN / 32;  // 32-key blocks per tile
   constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 domain)
-  // LDS reads issued ahead of their products (below); not in the 8-wave
-  // d = 128, 128-key configuration, which has no registers left for them.
-  constexpr bool AHEAD = !(D == 128 && BN == 128 && WAVES == 8);
+  // The default d = 64 configuration moves the reference max lazily, without
+  // a row max per tile (see softmax_pv); at d = 128 that measured no faster.
+  constexpr bool LAZY_MAX = D == 64 && BN == 64 && WAVES == 4;
+  // LDS reads issued ahead of their products (below). Not in the lazy d = 64
+  // configuration (they gained nothing at d = 64, and their registers would
+  // cost it the fourth wave per SIMD), nor in the 8-wave d = 128, 128-key
+  // configuration, which has no registers left for them.
+  constexpr bool AHEAD = !LAZY_MAX && !(D == 128 && BN == 128 && WAVES == 8);
+  constexpr float SUM_MAX = 256.0f;  // largest probability allowed against the reference (2^TAU)
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   // Two LDS stages for K and two for V, as four separate objects: the stage
   // of every access is a compile-time constant (the loop is unrolled by
@@ -170,24 +176,37 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
         for (int r = 0; r < 16; ++r)
           if (32 * mt + 8 * (r >> 2) + (r & 3) > lim) s[mt][r] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // Move the reference max to the tile's row max when that grows by more
+    // than TAU (slack > 0), or when it grows at all (slack = 0).
+    auto rebase = [&](float slack) __attribute__((always_inline)) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < NS; ++mt)
+      for (int mt = 0; mt < NS; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = xhalf_max(mx) * c;
-    const bool grow = mx > m_run + TAU;
-    const float m_new = grow ? mx : m_run;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = xhalf_max(mx) * c;
+      const bool grow = mx > m_run + slack;
+      const float m_new = grow ? mx : m_run;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+      m_run = m_new;
+    };
+    // d = 128: the row max of every tile. d = 64 (vector-bound): the
+    // exponentials of a k-step are taken against the current reference and
+    // the reference is moved only on a row's first tile and when a
+    // probability would exceed 2^TAU, which the sum of the k-step's eight
+    // values shows (a value above 2^TAU, an infinity or a NaN fails the test).
+    if constexpr (LAZY_MAX) {
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) rebase(0.f);
+    } else {
+      rebase(TAU);
     }
-    m_run = m_new;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
     // P^T as B operand: slot i of half h2 in k-step kk is key
     // 16*kk + 8*(i/4) + 4*h2 + i%4, i.e. value r = 8*(kk%2) + i of block kk/2.
     // V^T fragments are read one k-step ahead: the reads of k-step kk + 1
@@ -217,9 +236,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
       const f32x16& t = s[kk >> 1];
       const int r0 = 8 * (kk & 1);
       float e[8];
+      auto exps = [&]() __attribute__((always_inline)) {
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(t[r0 + i], c, -m_use));
-      l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(t[r0 + i], c, -m_use));
+        return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      };
+      float esum = exps();
+      if constexpr (LAZY_MAX) {
+        if (__builtin_amdgcn_ballot_w64(!(esum <= SUM_MAX)) != 0) {
+          rebase(0.f);
+          esum = exps();
+        }
+      }
+      l_run += esum;
       if (DROP) {
         // Dropout after the row sum (the softmax is of the undropped row):
         // slots 0-3 are keys kd .. kd+3 and slots 4-7 keys kd+8 .. kd+11,
