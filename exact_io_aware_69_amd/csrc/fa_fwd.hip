@@ -29,7 +29,10 @@
 //   * The reference max used in the exponent is only moved when a row max
 //     grows by more than 2^8 (in the exp2 domain); until then the
 //     accumulator is not rescaled. The result is unchanged because O and l
-//     share the reference; fp32 holds the at most 256x larger terms.
+//     share the reference; fp32 holds the at most 256x larger terms. The
+//     default d = 64 tiles do not even take the row max of every tile: they
+//     test each k-step's sum of probabilities against 2^8 instead, and take
+//     the row max only when that test fails or on a row's first tile.
 #include <type_traits>
 
 #include "fa_device.h"
