@@ -119,7 +119,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0, max_s: float = 30.0):
     B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
     scale = 1.0 / math.sqrt(d)
     mask = inp.get("mask")
-    done, flops, t_total = 0, 0.0, 0.0
+    done, flops, performed, t_total = 0, 0.0, 0.0, 0.0
     heads = [(b, h) for b in range(B) for h in range(H)]
     for (b, h) in heads:
         Q, K, V = (oracle.widen_bf16(inp[n][b, h]) for n in ("q", "k", "v"))
@@ -131,13 +131,18 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0, max_s: float = 30.0):
             dO = oracle.widen_bf16(inp["do"][b, h])
             oracle.head_backward(Q, K, V, dO, causal, scale, mh)
             f = 3.5 * f_fwd
+            # products the oracle computes over all N x N entries: Q K^T and P V
+            # in its forward, then Q K^T, P^T dO, dO V^T, dS K and dS^T Q
+            fp = 14.0 * N * N * d
         else:
             for r0 in range(0, N, 1024):
                 oracle.head_forward(Q, K, V, causal, scale, mh, rows=np.arange(r0, min(N, r0 + 1024)))
             f = f_fwd
+            fp = 4.0 * N * N * d
         dt = time.perf_counter() - t0
         t_total += dt
         flops += f
+        performed += fp
         done += 1
         if t_total >= budget_s or t_total + dt > max_s:
             break
@@ -149,6 +154,9 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0, max_s: float = 30.0):
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, {what} of {done} whole head(s) (b, h) of this workload at full N={N}, "
                   f"{t_total:.1f} s; algorithmic FLOPs of the sample / wall time",
+        # the same run on the FLOPs the oracle performs (it materialises every
+        # score and skips nothing)
+        "value_performed_flops": performed / t_total / 1e12,
     }
 
 
