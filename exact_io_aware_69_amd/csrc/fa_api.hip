@@ -55,7 +55,13 @@ size_t workspace_half(int B, int H, int N) {
   const size_t rows = (size_t)B * H * padded_rows(N);
   return (rows * sizeof(float) + 255) & ~(size_t)255;
 }
-size_t workspace_bytes_for(int B, int H, int N) { return 2 * workspace_half(B, H, N); }
+// Block-sparse schedule: per head, sparse_kslots(nb) key-tile and nb
+// query-tile int32 entries (fa_params.h).
+size_t schedule_bytes(int H, int N) {
+  const size_t nb = (size_t)(N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK;
+  return ((size_t)H * (fa::sparse_kslots((int)nb) + nb) * sizeof(int) + 255) & ~(size_t)255;
+}
+size_t workspace_bytes_for(int B, int H, int N) { return 2 * workspace_half(B, H, N) + schedule_bytes(H, N); }
 
 // Dropout arguments -> generator parameters; p must lie in [0, 1).
 int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* dr) {
@@ -123,6 +129,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   p.dv = static_cast<uint16_t*>(dv);
   p.Dneg = static_cast<float*>(workspace);
   p.lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + workspace_half(B, H, N));
+  p.korder = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + 2 * workspace_half(B, H, N));
+  p.qorder = p.korder + (size_t)H * fa::sparse_kslots((N + fa::MASK_BLOCK - 1) / fa::MASK_BLOCK);
   p.mask = mask;
   p.visited_kv = visited_kv;
   p.visited_q = visited_q;

@@ -148,9 +148,15 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   const int n_qt = (p.N + BMQ - 1) / BMQ;
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   // Ascending key tiles: under causal the first ones see the most queries.
+  // Block-sparse: the schedule's key tile of this rank (the grid has a slot
+  // for two tiles per mask block; slots past the last tile have no work).
   int bh, jt;
-  head_rank_order(lid, n_kt, p.hgrp, bh, jt);
+  head_rank_order(lid, SPARSE ? p.nb * (MASK_BLOCK / BNK) : n_kt, p.hgrp, bh, jt);
   const int h = bh % p.H;
+  if (SPARSE) {
+    jt = p.korder[(size_t)h * sparse_kslots(p.nb) + jt];
+    if (jt < 0 || jt >= n_kt) return;  // whole workgroup, before any barrier
+  }
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
   const int kb = jt * BNK;
@@ -549,8 +555,11 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   const int lid = xcd_grouped_block(blockIdx.x, gridDim.x);
   int bh, qt;
   head_rank_order(lid, n_qt, p.hgrp, bh, qt);
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest query tiles first
   const int h = bh % p.H;
+  if (SPARSE)
+    qt = min(max(p.qorder[(size_t)h * p.nb + qt], 0), n_qt - 1);  // the schedule's tile of this rank
+  else if (CAUSAL)
+    qt = n_qt - 1 - qt;  // longest query tiles first
   const int N = p.N;
   const size_t head = (size_t)bh * N * D;
   const int q_lo = qt * BM;
@@ -710,6 +719,47 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ block-sparse schedule
+// One workgroup per head: the work of each key tile (mask blocks of its
+// column that some query sees) and of each query tile (blocks of its row),
+// then a stable ranking by falling work, so that the dK/dV and dQ launches
+// start their longest tiles first (the tail of a launch is then made of
+// short tiles). tpb = key tiles per mask block (1 or 2). Up to
+// SCHED_MAX_NB blocks per row; larger masks keep the plain order.
+__global__ __launch_bounds__(256) void fa_bwd_sched_kernel(const uint8_t* __restrict__ mask, int* __restrict__ korder,
+                                                           int* __restrict__ qorder, int nb, int tpb, int causal) {
+  __shared__ int kw[SCHED_MAX_NB];
+  __shared__ int qw[SCHED_MAX_NB];
+  const int h = blockIdx.x;
+  const uint8_t* m = mask + (size_t)h * nb * nb;
+  int* ko = korder + (size_t)h * sparse_kslots(nb);
+  int* qo = qorder + (size_t)h * nb;
+  if (nb > SCHED_MAX_NB) {
+    for (int i = threadIdx.x; i < nb; i += 256) {
+      qo[i] = i;
+      for (int t = 0; t < tpb; ++t) ko[i * tpb + t] = i * tpb + t;
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < nb; i += 256) {
+    int kc = 0, qc = 0;
+    for (int r = 0; r < nb; ++r) kc += (m[(size_t)r * nb + i] != 0 && (!causal || r >= i)) ? 1 : 0;
+    for (int c = 0; c < nb; ++c) qc += (m[(size_t)i * nb + c] != 0 && (!causal || c <= i)) ? 1 : 0;
+    kw[i] = kc;
+    qw[i] = qc;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += 256) {
+    int rk = 0, rq = 0;
+    for (int j = 0; j < nb; ++j) {
+      rk += (kw[j] > kw[i] || (kw[j] == kw[i] && j < i)) ? 1 : 0;
+      rq += (qw[j] > qw[i] || (qw[j] == qw[i] && j < i)) ? 1 : 0;
+    }
+    qo[rq] = i;
+    for (int t = 0; t < tpb; ++t) ko[rk * tpb + t] = i * tpb + t;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
@@ -721,17 +771,25 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
                        p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (SPARSE) {
+      hipLaunchKernelGGL(fa_bwd_sched_kernel, dim3((unsigned)p.H), dim3(256), 0, st,
+                         p.mask, p.korder, p.qorder, p.nb, MASK_BLOCK / bwd_kv_bn<D>(), (int)CAUSAL);
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
+    }
   }
-  // Dense causal launches interleave heads (see head_group); block-sparse
-  // work per tile depends on the mask, so those keep head order.
-  constexpr bool INTERLEAVE = CAUSAL && !SPARSE;
+  // Dense causal launches interleave heads (see head_group), as do
+  // block-sparse ones, whose tiles the schedule orders by falling work.
+  constexpr bool INTERLEAVE = CAUSAL || SPARSE;
   if (stages & 2) {
     const int n_kt1 = (p.N + bwd_kv_bn<D>() - 1) / bwd_kv_bn<D>();
+    // Block-sparse: one slot per (mask block, key tile of the block).
+    const int slots = SPARSE ? p.nb * (MASK_BLOCK / bwd_kv_bn<D>()) : n_kt1;
     const auto kernel = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
     static const int wgs = wgs_per_cu((const void*)kernel, 64 * bwd_kv_waves<D>());
     BwdParams q = p;
-    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, n_kt1) : 1;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * n_kt1)), dim3(64 * bwd_kv_waves<D>()), 0, st, q);
+    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, slots) : 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * slots)), dim3(64 * bwd_kv_waves<D>()), 0, st, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -85,7 +85,19 @@ struct BwdParams {
   float dfac;   // factor on -D in the workspace: 1, or 1 - p with dropout
   Dropout drop;  // used by the dropout instantiations only
   int hgrp;      // heads per dispatch group (head_rank_order), set per launch
+  // Block-sparse schedule in the workspace (written by the preprocess stage):
+  // per head, the key tiles (korder, SPARSE_KSLOTS(nb) entries) and the
+  // query tiles (qorder, nb entries) in order of falling work.
+  int* korder;
+  int* qorder;
 };
+
+// Key-tile slots per head in the block-sparse schedule: two per mask block,
+// enough for 64-key tiles (128-key tiles use the first nb).
+__host__ __device__ inline int sparse_kslots(int nb) { return 2 * nb; }
+// Mask blocks per row up to which the schedule is sorted (larger masks keep
+// the plain order).
+constexpr int SCHED_MAX_NB = 2048;
 
 // (head, tile rank) of logical workgroup `lid` in a grid of heads x
 // `ntile` tiles, ordered in groups of G consecutive heads (G divides the

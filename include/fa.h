@@ -131,8 +131,11 @@ int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, int seq_groups,
                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need:
- * float32 D = rowsum(dO * O) for every row, O(B*H*N) -- never O(N^2). */
+/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need, O(B*H*N) --
+ * never O(N^2): float32 D = rowsum(dO * O) and lse * log2(e) for every row
+ * (rows padded to 128 per head), then, for block-sparse calls, a schedule of
+ * three int32 per (head, 128-row mask block): the key and query tiles of
+ * each head in order of falling work, which the preprocess stage writes. */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 
 /* Backward. Inputs: q, k, v, the forward's o and lse, and the upstream

@@ -60,10 +60,13 @@ def test_tile_config():
 
 
 def test_workspace_size_is_linear_in_N():
-    # two fp32 values (D and lse * log2 e) per row, rows padded to 128 per head
+    # two fp32 values (D and lse * log2 e) per row, rows padded to 128 per
+    # head, plus the block-sparse schedule: three int32 per (head, 128-row
+    # mask block)
     st, a = _lib.fa_bwd_workspace_size(2, 16, 8192, 64)
-    assert st == 0 and a >= 2 * 16 * 8192 * 8 and a < 2 * 16 * 8192 * 8 + 512
-    assert _lib.fa_bwd_workspace_size(1, 1, 1, 64)[1] >= 128 * 8
+    sched = 16 * 3 * 64 * 4
+    assert st == 0 and a >= 2 * 16 * 8192 * 8 + sched and a < 2 * 16 * 8192 * 8 + sched + 768
+    assert _lib.fa_bwd_workspace_size(1, 1, 1, 64)[1] >= 128 * 8 + 3 * 4
     st, b = _lib.fa_bwd_workspace_size(2, 16, 16384, 64)
     assert b == 2 * a
     assert _lib.fa_bwd_workspace_size(0, 1, 1, 64)[0] == -2
