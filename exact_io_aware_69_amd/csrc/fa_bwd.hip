@@ -728,35 +728,79 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
 // SCHED_MAX_NB blocks per row; larger masks keep the plain order.
 __global__ __launch_bounds__(256) void fa_bwd_sched_kernel(const uint8_t* __restrict__ mask, int* __restrict__ korder,
                                                            int* __restrict__ qorder, int nb, int tpb, int causal) {
-  __shared__ int kw[SCHED_MAX_NB];
-  __shared__ int qw[SCHED_MAX_NB];
+  __shared__ int kw[SCHED_MAX_NB];  // work of each key block (kept blocks of its column)
+  __shared__ int qw[SCHED_MAX_NB];  // work of each query block (kept blocks of its row)
+  __shared__ int kr[SCHED_MAX_NB];  // rank of each key block
+  __shared__ int qr[SCHED_MAX_NB];  // rank of each query block
   const int h = blockIdx.x;
+  const int tid = (int)threadIdx.x;
   const uint8_t* m = mask + (size_t)h * nb * nb;
   int* ko = korder + (size_t)h * sparse_kslots(nb);
   int* qo = qorder + (size_t)h * nb;
   if (nb > SCHED_MAX_NB) {
-    for (int i = threadIdx.x; i < nb; i += 256) {
+    for (int i = tid; i < nb; i += 256) {
       qo[i] = i;
       for (int t = 0; t < tpb; ++t) ko[i * tpb + t] = i * tpb + t;
     }
     return;
   }
-  for (int i = threadIdx.x; i < nb; i += 256) {
-    int kc = 0, qc = 0;
-    for (int r = 0; r < nb; ++r) kc += (m[(size_t)r * nb + i] != 0 && (!causal || r >= i)) ? 1 : 0;
-    for (int c = 0; c < nb; ++c) qc += (m[(size_t)i * nb + c] != 0 && (!causal || c <= i)) ? 1 : 0;
-    kw[i] = kc;
-    qw[i] = qc;
+  for (int i = tid; i < nb; i += 256) {
+    kw[i] = 0;
+    qw[i] = 0;
+    kr[i] = 0;
+    qr[i] = 0;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nb; i += 256) {
-    int rk = 0, rq = 0;
-    for (int j = 0; j < nb; ++j) {
-      rk += (kw[j] > kw[i] || (kw[j] == kw[i] && j < i)) ? 1 : 0;
-      rq += (qw[j] > qw[i] || (qw[j] == qw[i] && j < i)) ? 1 : 0;
+  // Both passes walk the nb x nb elements with consecutive threads on
+  // consecutive columns; (row, column) of element e advance by
+  // (256 / nb, 256 % nb) per step of 256.
+  const int nn = nb * nb;
+  const int dr = 256 / nb, dc = 256 % nb;
+  auto advance = [&](int& r, int& c) __attribute__((always_inline)) {
+    r += dr;
+    c += dc;
+    if (c >= nb) {
+      c -= nb;
+      ++r;
     }
-    qo[rq] = i;
-    for (int t = 0; t < tpb; ++t) ko[rk * tpb + t] = i * tpb + t;
+  };
+  // Work: a kept (and, under causal, visible) block adds to its row's and
+  // its column's count. Sixteen loads in flight per thread.
+  {
+    int r = tid / nb, c = tid % nb;
+    for (int e0 = 0; e0 < nn; e0 += 16 * 256) {
+      uint8_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + u * 256 + tid;
+        v[u] = e < nn ? m[e] : (uint8_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (v[u] != 0 && (!causal || c <= r)) {
+          atomicAdd(&kw[c], 1);
+          atomicAdd(&qw[r], 1);
+        }
+        advance(r, c);
+      }
+    }
+  }
+  __syncthreads();
+  // Rank by falling work, ties by index: element (j, i) adds one to the rank
+  // of block i when block j comes before it.
+  {
+    int j = tid / nb, i = tid % nb;
+    for (int e = tid; e < nn; e += 256) {
+      const int wi = kw[i], wj = kw[j], vi = qw[i], vj = qw[j];
+      if (wj > wi || (wj == wi && j < i)) atomicAdd(&kr[i], 1);
+      if (vj > vi || (vj == vi && j < i)) atomicAdd(&qr[i], 1);
+      advance(j, i);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) {
+    qo[qr[i]] = i;
+    for (int t = 0; t < tpb; ++t) ko[kr[i] * tpb + t] = i * tpb + t;
   }
 }
 
