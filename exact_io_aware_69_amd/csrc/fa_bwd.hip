@@ -41,12 +41,114 @@ namespace fa {
 // at close to the HBM rate.
 constexpr int PRE_ROWS = 4;
 
-template <int D>
+// ------------------------------------------------------------------ block-sparse schedule
+// One workgroup per head (run by the first H workgroups of the preprocess
+// launch, alongside its rows): the work of each key tile (mask blocks of its
+// column that some query sees) and of each query tile (blocks of its row),
+// then a stable ranking by falling work, so that the dK/dV and dQ launches
+// start their longest tiles first (the tail of a launch is then made of
+// short tiles). tpb = key tiles per mask block (1 or 2). Up to
+// SCHED_MAX_NB blocks per row; larger masks keep the plain order.
+__device__ __forceinline__ void bwd_sched_head(const uint8_t* __restrict__ mask, int* __restrict__ korder,
+                                               int* __restrict__ qorder, int nb, int tpb, int causal, int h) {
+  __shared__ int kw[SCHED_MAX_NB];  // work of each key block (kept blocks of its column)
+  __shared__ int qw[SCHED_MAX_NB];  // work of each query block (kept blocks of its row)
+  __shared__ int kr[SCHED_MAX_NB];  // rank of each key block
+  __shared__ int qr[SCHED_MAX_NB];  // rank of each query block
+  const int tid = (int)threadIdx.x;
+  const uint8_t* m = mask + (size_t)h * nb * nb;
+  int* ko = korder + (size_t)h * sparse_kslots(nb);
+  int* qo = qorder + (size_t)h * nb;
+  if (nb > SCHED_MAX_NB) {
+    for (int i = tid; i < nb; i += 256) {
+      qo[i] = i;
+      for (int t = 0; t < tpb; ++t) ko[i * tpb + t] = i * tpb + t;
+    }
+    return;
+  }
+  for (int i = tid; i < nb; i += 256) {
+    kw[i] = 0;
+    qw[i] = 0;
+    kr[i] = 0;
+    qr[i] = 0;
+  }
+  __syncthreads();
+  // Both passes walk the nb x nb elements with consecutive threads on
+  // consecutive columns; (row, column) of element e advance by
+  // (256 / nb, 256 % nb) per step of 256.
+  const int nn = nb * nb;
+  const int dr = 256 / nb, dc = 256 % nb;
+  auto advance = [&](int& r, int& c) __attribute__((always_inline)) {
+    r += dr;
+    c += dc;
+    if (c >= nb) {
+      c -= nb;
+      ++r;
+    }
+  };
+  // Work: a kept (and, under causal, visible) block adds to its row's and
+  // its column's count. Sixteen loads in flight per thread.
+  {
+    int r = tid / nb, c = tid % nb;
+    for (int e0 = 0; e0 < nn; e0 += 16 * 256) {
+      uint8_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + u * 256 + tid;
+        v[u] = e < nn ? m[e] : (uint8_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (v[u] != 0 && (!causal || c <= r)) {
+          atomicAdd(&kw[c], 1);
+          atomicAdd(&qw[r], 1);
+        }
+        advance(r, c);
+      }
+    }
+  }
+  __syncthreads();
+  // Rank by falling work, ties by index: element (j, i) adds one to the rank
+  // of block i when block j comes before it.
+  {
+    int j = tid / nb, i = tid % nb;
+    for (int e = tid; e < nn; e += 256) {
+      const int wi = kw[i], wj = kw[j], vi = qw[i], vj = qw[j];
+      if (wj > wi || (wj == wi && j < i)) atomicAdd(&kr[i], 1);
+      if (vj > vi || (vj == vi && j < i)) atomicAdd(&qr[i], 1);
+      advance(j, i);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nb; i += 256) {
+    qo[qr[i]] = i;
+    for (int t = 0; t < tpb; ++t) ko[kr[i] * tpb + t] = i * tpb + t;
+  }
+}
+
+struct SchedArgs {
+  const uint8_t* mask;
+  int* korder;
+  int* qorder;
+  int nb, tpb, causal, heads;  // heads = workgroups that build the schedule (one per head)
+};
+
+template <int D, bool SCHED>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dO,
                                                          const float* __restrict__ lse,
                                                          float* __restrict__ Dneg, float* __restrict__ lse2,
-                                                         int N, int Npad, size_t rows_pad, float dfac) {
+                                                         int N, int Npad, size_t rows_pad, float dfac,
+                                                         const SchedArgs sa) {
+  if (SCHED) {
+    // Block-sparse: the first sa.heads workgroups build the schedule, the
+    // rest run the preprocess rows.
+    if ((int)blockIdx.x < sa.heads) {
+      bwd_sched_head(sa.mask, sa.korder, sa.qorder, sa.nb, sa.tpb, sa.causal, (int)blockIdx.x);
+      return;
+    }
+  }
+  const unsigned bid = SCHED ? blockIdx.x - (unsigned)sa.heads : blockIdx.x;
   constexpr int CH = D / 8;      // lanes per row, 8 elements each
   constexpr int RPB = 256 / CH;  // rows per workgroup and pass
   const int c = threadIdx.x % CH;
@@ -55,7 +157,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restr
   u32x4 a[PRE_ROWS], b[PRE_ROWS];
 #pragma unroll
   for (int i = 0; i < PRE_ROWS; ++i) {
-    prow[i] = (size_t)blockIdx.x * (RPB * PRE_ROWS) + (size_t)i * RPB + threadIdx.x / CH;
+    prow[i] = (size_t)bid * (RPB * PRE_ROWS) + (size_t)i * RPB + threadIdx.x / CH;
     const size_t bh = prow[i] / Npad;
     const int r = (int)(prow[i] - bh * Npad);
     real[i] = prow[i] < rows_pad && r < N;
@@ -719,91 +821,6 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ block-sparse schedule
-// One workgroup per head: the work of each key tile (mask blocks of its
-// column that some query sees) and of each query tile (blocks of its row),
-// then a stable ranking by falling work, so that the dK/dV and dQ launches
-// start their longest tiles first (the tail of a launch is then made of
-// short tiles). tpb = key tiles per mask block (1 or 2). Up to
-// SCHED_MAX_NB blocks per row; larger masks keep the plain order.
-__global__ __launch_bounds__(256) void fa_bwd_sched_kernel(const uint8_t* __restrict__ mask, int* __restrict__ korder,
-                                                           int* __restrict__ qorder, int nb, int tpb, int causal) {
-  __shared__ int kw[SCHED_MAX_NB];  // work of each key block (kept blocks of its column)
-  __shared__ int qw[SCHED_MAX_NB];  // work of each query block (kept blocks of its row)
-  __shared__ int kr[SCHED_MAX_NB];  // rank of each key block
-  __shared__ int qr[SCHED_MAX_NB];  // rank of each query block
-  const int h = blockIdx.x;
-  const int tid = (int)threadIdx.x;
-  const uint8_t* m = mask + (size_t)h * nb * nb;
-  int* ko = korder + (size_t)h * sparse_kslots(nb);
-  int* qo = qorder + (size_t)h * nb;
-  if (nb > SCHED_MAX_NB) {
-    for (int i = tid; i < nb; i += 256) {
-      qo[i] = i;
-      for (int t = 0; t < tpb; ++t) ko[i * tpb + t] = i * tpb + t;
-    }
-    return;
-  }
-  for (int i = tid; i < nb; i += 256) {
-    kw[i] = 0;
-    qw[i] = 0;
-    kr[i] = 0;
-    qr[i] = 0;
-  }
-  __syncthreads();
-  // Both passes walk the nb x nb elements with consecutive threads on
-  // consecutive columns; (row, column) of element e advance by
-  // (256 / nb, 256 % nb) per step of 256.
-  const int nn = nb * nb;
-  const int dr = 256 / nb, dc = 256 % nb;
-  auto advance = [&](int& r, int& c) __attribute__((always_inline)) {
-    r += dr;
-    c += dc;
-    if (c >= nb) {
-      c -= nb;
-      ++r;
-    }
-  };
-  // Work: a kept (and, under causal, visible) block adds to its row's and
-  // its column's count. Sixteen loads in flight per thread.
-  {
-    int r = tid / nb, c = tid % nb;
-    for (int e0 = 0; e0 < nn; e0 += 16 * 256) {
-      uint8_t v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = e0 + u * 256 + tid;
-        v[u] = e < nn ? m[e] : (uint8_t)0;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (v[u] != 0 && (!causal || c <= r)) {
-          atomicAdd(&kw[c], 1);
-          atomicAdd(&qw[r], 1);
-        }
-        advance(r, c);
-      }
-    }
-  }
-  __syncthreads();
-  // Rank by falling work, ties by index: element (j, i) adds one to the rank
-  // of block i when block j comes before it.
-  {
-    int j = tid / nb, i = tid % nb;
-    for (int e = tid; e < nn; e += 256) {
-      const int wi = kw[i], wj = kw[j], vi = qw[i], vj = qw[j];
-      if (wj > wi || (wj == wi && j < i)) atomicAdd(&kr[i], 1);
-      if (vj > vi || (vj == vi && j < i)) atomicAdd(&qr[i], 1);
-      advance(j, i);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < nb; i += 256) {
-    qo[qr[i]] = i;
-    for (int t = 0; t < tpb; ++t) ko[kr[i] * tpb + t] = i * tpb + t;
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 // stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
@@ -811,16 +828,12 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
   if (stages & 1) {
     const size_t rows_pad = (size_t)BH * p.Npad;
     constexpr int RPB = 256 / (D / 8) * PRE_ROWS;  // rows per workgroup
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows_pad + RPB - 1) / RPB)), dim3(256), 0, st, p.o,
-                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac);
+    const unsigned pre_wgs = (unsigned)((rows_pad + RPB - 1) / RPB);
+    const SchedArgs sa{p.mask, p.korder, p.qorder, p.nb, MASK_BLOCK / bwd_kv_bn<D>(), (int)CAUSAL, SPARSE ? p.H : 0};
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<D, SPARSE>), dim3(pre_wgs + (unsigned)sa.heads), dim3(256), 0, st, p.o,
+                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac, sa);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (SPARSE) {
-      hipLaunchKernelGGL(fa_bwd_sched_kernel, dim3((unsigned)p.H), dim3(256), 0, st,
-                         p.mask, p.korder, p.qorder, p.nb, MASK_BLOCK / bwd_kv_bn<D>(), (int)CAUSAL);
-      const hipError_t e2 = hipGetLastError();
-      if (e2 != hipSuccess) return e2;
-    }
   }
   // Dense causal launches interleave heads (see head_group), as do
   // block-sparse ones, whose tiles the schedule orders by falling work.
