@@ -8,7 +8,8 @@ dK/dV, dQ), all through the C ABI of libfa.so, inputs resident in HBM.
 Default workload: causal attention, B=4, H=16, N=4096, d=128, bf16 inputs
 drawn i.i.d. N(0,1) from seed 0, forward + backward -- the causal d=128
 N>=4k case the headline figure (attention TFLOP/s, fwd and fwd+bwd, % of
-the bf16 MFMA peak) is stated for. Other workloads: --workload.
+the bf16 MFMA peak) is stated for. Other workloads: --workload, a named one
+or any shape written KIND_bB_hH_nN_dD_PASS (e.g. causal_b2_h16_n8192_d128_fwdbwd).
 
 FLOP model: forward 4*B*H*N^2*d, halved for causal; backward 2.5x forward.
 Block-sparse counts kept 128x128 blocks only (a diagonal block counts 1/2
@@ -29,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -52,6 +54,30 @@ WORKLOADS = {
     "dense_b1_h2_n256_d64_fwd": dict(B=1, H=2, N=256, d=64, causal=False, sparse=False, bwd=False),
 }
 DEFAULT = "causal_b4_h16_n4096_d128_fwdbwd"
+WORKLOAD_RE = re.compile(r"^(dense|causal|blocksparse)_b(\d+)_h(\d+)_n(\d+)_d(64|128)_(fwd|fwdbwd)$")
+
+
+def workload_config(name: str) -> dict:
+    """Shape and flags of a workload: a named one above, or any name of the
+    same form, KIND_bB_hH_nN_dD_PASS with KIND dense, causal or blocksparse
+    and PASS fwd or fwdbwd (synthetic inputs of that shape)."""
+    if name in WORKLOADS:
+        return dict(WORKLOADS[name])
+    m = WORKLOAD_RE.match(name)
+    if not m:
+        raise argparse.ArgumentTypeError(
+            f"unknown workload {name!r}: one of {', '.join(sorted(WORKLOADS))}, or "
+            "KIND_bB_hH_nN_dD_PASS (KIND dense|causal|blocksparse, D 64|128, PASS fwd|fwdbwd)")
+    kind, B, H, N, d, pss = m.groups()
+    if min(int(B), int(H), int(N)) < 1:
+        raise argparse.ArgumentTypeError(f"workload {name!r}: B, H and N must be at least 1")
+    return dict(B=int(B), H=int(H), N=int(N), d=int(d), causal=kind == "causal", sparse=kind == "blocksparse",
+                bwd=pss == "fwdbwd")
+
+
+def _workload_arg(name: str) -> str:
+    workload_config(name)
+    return name
 
 KERNEL_SOURCES = {
     "fwd": "fa_fwd.hip", "bwd_pre": "fa_bwd.hip", "bwd_dkdv": "fa_bwd.hip", "bwd_dq": "fa_bwd.hip",
@@ -165,7 +191,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, type=_workload_arg,
+                    help="one of " + ", ".join(sorted(WORKLOADS)) + "; or any KIND_bB_hH_nN_dD_PASS "
+                         "(KIND dense|causal|blocksparse, D 64|128, PASS fwd|fwdbwd)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--standard", action="store_true",
@@ -206,7 +234,7 @@ def main(argv=None):
         return 0
 
     _lib.lib()  # raises if libfa.so is missing: there is no other path
-    cfg = dict(WORKLOADS[args.workload])
+    cfg = workload_config(args.workload)
     if args.standard or args.fa1:
         cfg["bwd"] = False
     if args.fa1 and cfg["sparse"]:
