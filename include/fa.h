@@ -135,7 +135,9 @@ int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
  * never O(N^2): float32 D = rowsum(dO * O) and lse * log2(e) for every row
  * (rows padded to 128 per head), then, for block-sparse calls, a schedule of
  * three int32 per (head, 128-row mask block): the key and query tiles of
- * each head in order of falling work, which the preprocess stage writes. */
+ * each head in order of falling work, which the preprocess stage writes
+ * (masks of more than 2048 blocks per row keep the plain order). The order
+ * changes only which tiles run first, never the results. */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 
 /* Backward. Inputs: q, k, v, the forward's o and lse, and the upstream
