@@ -798,8 +798,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
         const bool need_mask = (jc * BN + BN > N) || (CAUSAL && jc * BN + BN - 1 > q0);
         tile(jc, kst[P], vst[P], need_mask);
       }
-      wait_vmem();
-      __syncthreads();
+      // After the last tile no copy is in flight and no LDS access follows;
+      // under causal masking each wave then goes on to its epilogue without
+      // waiting for the others, as in the forward kernel.
+      if (!CAUSAL || jn < kt_end) {
+        wait_vmem();
+        __syncthreads();
+      }
       jc = jn;
       return jn < kt_end;
     };

@@ -303,10 +303,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
         const bool need_mask = (jc * BN + BN > N) || (CAUSAL && jc * BN + BN - 1 > q0);
         softmax_pv(s, jc, vst[P], need_mask);
       }
-      // After the last tile no copy is in flight and no LDS access follows:
-      // each wave goes on to its epilogue without waiting for the others.
-      // (jn < kt_end is the same for every wave of the workgroup.)
-      if (jn < kt_end) {
+      // After the last tile no copy is in flight and no LDS access follows.
+      // Under causal masking the waves of the lower rows skip the last key
+      // tiles, so each wave goes on to its epilogue without waiting for the
+      // others (jn < kt_end is the same for every wave of the workgroup).
+      // Dense waves finish together and keep the barrier (measured faster).
+      if (!CAUSAL || jn < kt_end) {
         wait_vmem();
         __syncthreads();
       }
