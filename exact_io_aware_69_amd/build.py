@@ -15,6 +15,11 @@ import shutil
 import subprocess
 import sys
 
+try:
+    from . import _srcid
+except ImportError:  # run as a script
+    import _srcid
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
@@ -32,9 +37,12 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, build_id: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    # Only the C ABI's unit carries the source identity (fa_build_id), so the
+    # kernels' objects do not depend on it.
+    extra = [f'-DFA_BUILD_ID="{build_id}"'] if src == "fa_api.hip" else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -50,9 +58,10 @@ def build(verbose: bool = True) -> str:
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         raise RuntimeError("hipcc not found")
     os.makedirs(BUILD, exist_ok=True)
+    build_id = _srcid.source_id()
     workers = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, build_id), SOURCES))
     tmp = LIB + ".tmp"
     rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
@@ -62,7 +71,7 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (sources {build_id})")
     return LIB
 
 

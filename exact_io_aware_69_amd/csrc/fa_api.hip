@@ -279,6 +279,11 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed, uint32_
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+#ifndef FA_BUILD_ID
+#define FA_BUILD_ID "unknown"
+#endif
+const char* fa_build_id(void) { return FA_BUILD_ID; }
+
 int fa_tile_config(int pass, int d, int causal, int* bm, int* bn) {
   if (!bm || !bn) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;

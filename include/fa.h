@@ -33,8 +33,12 @@
  *     or NULL for the default stream. Work is only enqueued; nothing waits
  *     on the host. Outputs must not alias inputs.
  *   - Ownership: the caller allocates and frees every buffer, including the
- *     backward workspace. The library keeps no device memory and no global
- *     state between calls (fa_std_fwd aside: it keeps a rocBLAS handle).
+ *     backward workspace. The library keeps no device memory of its own and
+ *     no state that changes results. Per-process state it does keep: each
+ *     kernel's occupancy (workgroups per CU, asked of the runtime on the
+ *     first launch and cached, used only to pick the launch order of causal
+ *     and block-sparse grids) and, for fa_std_fwd, one rocBLAS handle per
+ *     device.
  *   - Errors: every entry point returns FA_OK (0) or a negative fa_status.
  *     Argument checks run before anything is enqueued; a failed launch is
  *     reported as FA_ERR_HIP. Faults during execution surface at the
@@ -132,7 +136,10 @@ int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need, O(B*H*N) --
- * never O(N^2): float32 D = rowsum(dO * O) and lse * log2(e) for every row
+ * never O(N^2) (FlashAttention-2 review, Abstract: memory linear instead of
+ * quadratic in sequence length; Stanford FlashAttention summary: only the
+ * softmax normalisation statistic is kept for the backward pass):
+ * float32 D = rowsum(dO * O) and lse * log2(e) for every row
  * (rows padded to 128 per head), then, for block-sparse calls, a schedule of
  * three int32 per (head, 128-row mask block): the key and query tiles of
  * each head in order of falling work, which the preprocess stage writes
@@ -151,14 +158,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H, int N, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward with a 128 x 128 block mask (same convention as the forward). */
+/* Backward with a 128 x 128 block mask (same convention as the forward);
+ * masked blocks are skipped in both backward kernels (Stanford
+ * FlashAttention summary, block-sparse FlashAttention). */
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        int B, int H, int N, int d, int causal, float scale,
                        const uint8_t* block_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* One backward kernel alone, so a caller can time or overlap them; fa_bwd
+/* One backward kernel alone, so a caller can time or overlap them (the
+ * three steps of the backward pass that recomputes attention on chip,
+ * Stanford FlashAttention summary, recomputation; the dK/dV and dQ steps
+ * are parallel over sequence length, FlashAttention-2 review, "Proposed
+ * method"); fa_bwd
  * (fa_bwd_blocksparse when block_mask != NULL) is exactly stages 0, 1, 2
  * enqueued in that order on one stream. stage 0: D = rowsum(dO * O) into
  * the workspace (reads o, dO); stage 1: dK and dV (reads q, k, v, lse, dO
@@ -200,11 +213,16 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    void* stream);
 /* The keep mask Z of the same generator, one byte (0 or 1) per element into
  * keep, a device buffer uint8 [B][H][N][N] owned by the caller (tests of
- * the generator; O(N^2) memory). */
+ * the generator; O(N^2) memory). The "PagedAttention" page names dropout
+ * only; the generator and its counter layout are this library's reading
+ * (Philox4x32-10, see fa_fwd_dropout). */
 int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed,
                     uint32_t offset, uint8_t* keep, void* stream);
 
 /* Tile sizes the kernels use, so a caller can size the visit maps below.
+ * A utility of this library: no passage of the pages defines it (they fix
+ * no tile sizes). Returns FA_ERR_UNSUPPORTED_D for d not in {64, 128},
+ * FA_ERR_SHAPE for a pass outside 0..2, FA_ERR_NULL for a NULL output.
  * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel;
  * causal: nonzero for the causal kernels (the d = 128 dQ kernel streams
  * 64-key tiles when causal, 32-key tiles otherwise). bm = query rows per
@@ -212,7 +230,12 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed,
 int fa_tile_config(int pass, int d, int causal, int* bm, int* bn);
 
 /* Debug forward: same computation as fa_fwd_blocksparse (block_mask may be
- * NULL for dense) and additionally writes visited, uint8
+ * NULL for dense) and additionally writes which tiles were skipped, so the
+ * skip decisions can be checked bit for bit: whole key tiles past the
+ * diagonal under causal masking (FlashAttention-2 review, "Proposed
+ * method": blocks that causal masking zeroes are not computed) and masked
+ * blocks of a block-sparse mask (Stanford FlashAttention summary,
+ * block-sparse FlashAttention: masked blocks are skipped). It writes visited, uint8
  * [B][H][ceil(N/bm)][ceil(N/bn)] (pass 0 tile sizes): 1 where the kernel
  * processed the (query tile, key tile) pair, 0 where it skipped it. The
  * caller zeroes `visited` before the call. */
@@ -221,7 +244,10 @@ int fa_fwd_debug_visits(const void* q, const void* k, const void* v, void* o, fl
                         const uint8_t* block_mask, uint8_t* visited, void* stream);
 
 /* Debug backward: same computation as fa_bwd_blocksparse (block_mask may be
- * NULL) and writes visited_kv, uint8 [B][H][ceil(N/bn1)][ceil(N/bm1)] (pass 1
+ * NULL), with the skip decisions of the backward kernels made visible (same
+ * passages as fa_fwd_debug_visits: causal block skipping, FlashAttention-2
+ * review, "Proposed method"; block-sparse skipping, Stanford FlashAttention
+ * summary). It writes visited_kv, uint8 [B][H][ceil(N/bn1)][ceil(N/bm1)] (pass 1
  * tile sizes, key tile major) from the dK/dV kernel and visited_q, uint8
  * [B][H][ceil(N/bm2)][ceil(N/bn2)] (pass 2 tile sizes) from the dQ kernel.
  * The caller zeroes both maps. */
@@ -232,7 +258,16 @@ int fa_bwd_debug_visits(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes,
                         uint8_t* visited_kv, uint8_t* visited_q, void* stream);
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Identity of the sources this library was built from: the first 16 hex
+ * digits of a SHA-256 over the kernel sources, the headers and the build
+ * script, fixed at build time (static string, never NULL). A utility of
+ * this library, which no passage of the pages defines: the Python binding
+ * recomputes it from the sources beside the library and refuses to load a
+ * library built from other sources. */
+const char* fa_build_id(void);
+
+/* Human-readable name of a status code (static string, never NULL). A
+ * utility of this library: no passage of the pages defines it. */
 const char* fa_status_str(int status);
 
 #ifdef __cplusplus

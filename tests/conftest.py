@@ -12,10 +12,17 @@ def pytest_configure(config):
 
 
 def _ensure_library():
-    """Build libfa.so only when nothing is built (a stale library is the
-    caller's business: run ``python -m exact_io_aware_69_amd.build``)."""
-    from exact_io_aware_69_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
+    """Build libfa.so when nothing is built or when the built library's
+    source identity (fa_build_id) differs from the sources in the tree, so
+    the tests never run a stale binary."""
+    from exact_io_aware_69_amd import _lib, _srcid
+    stale = not os.path.exists(_lib.LIB_PATH)
+    if not stale:
+        # The identity is a string constant inside the library; looking for
+        # it in the file avoids loading a library that may be replaced.
+        with open(_lib.LIB_PATH, "rb") as f:
+            stale = _srcid.source_id().encode() not in f.read()
+    if stale:
         from exact_io_aware_69_amd import build
         build.build()
 

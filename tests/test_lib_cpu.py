@@ -215,3 +215,29 @@ def test_dropout_argument_errors():
     assert _lib.fa_dropout_keep(1, 1, 0, 0.5, 1, 0, FAKE, None) == -2
     assert _lib.fa_dropout_keep(1, 1, 8, -1.0, 1, 0, FAKE, None) == -9
     assert "dropout" in _lib.fa_status_str(-9)
+
+
+def test_build_id_matches_sources():
+    from exact_io_aware_69_amd import _srcid
+    assert _lib.fa_build_id() == _srcid.source_id()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    from exact_io_aware_69_amd import _srcid
+    monkeypatch.setattr(_srcid, "source_id", lambda: "0000000000000000")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.StaleLibraryError):
+        _lib.lib()
+
+
+def test_every_declaration_cites_a_passage_or_says_none():
+    """Each entry point's comment block names the page passage that defines
+    its operation, or states that no passage defines it."""
+    text = open(HEADER).read()
+    cites = ("FlashAttention-2 review", "Stanford FlashAttention summary", "PagedAttention",
+             "no passage", "callers that cannot allocate")
+    for name in declared_functions():
+        pos = re.search(r"^\s*(?:int|const char\*)\s+" + name + r"\s*\(", text, flags=re.M).start()
+        block = text[text.rfind("/*", 0, pos):text.rfind("*/", 0, pos) + 2]
+        flat = " ".join(w for w in block.split() if w != "*")
+        assert any(c in flat for c in cites), (name, flat[:200])
