@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fa_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "fa_bwd_blocksparse": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
+    "fa_bwd_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]),
     "fa_bwd_stage": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _sz, _p]),
     "fa_fwd_dropout": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _f, _u64, _u32, _p]),
     "fa_bwd_dropout": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _f, _u64, _u32, _p, _sz,
@@ -148,6 +149,10 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scal
                        workspace_bytes, stream):
     return lib().fa_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale,
                                     block_mask, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, stream):
+    return lib().fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale, block_mask, stream)
 
 
 def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, workspace,

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -149,6 +150,41 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- fa_bwd_noalloc
+// The backward's scratch (D and lse * log2(e) per row, the block-sparse
+// schedule) for callers that cannot allocate: one file-scope device array.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with the
+// device current) and only that address is handed to the kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (FA_ERR_HIP if the
+// runtime cannot tell).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return FA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +272,25 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                        const uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, true, workspace,
                   workspace_bytes, nullptr, nullptr, 7, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                   const uint8_t* block_mask, void* stream) {
+  // Every argument check, the scratch limit included, comes before the
+  // first HIP call.
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (workspace_bytes_for(B, H, N) > kNoallocScratchBytes) return FA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, block_mask, block_mask != nullptr, ws,
+                  kNoallocScratchBytes, nullptr, nullptr, 7, stream);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -167,6 +167,26 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                        const uint8_t* block_mask,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same computation, arguments and results as
+ * fa_bwd_blocksparse (block_mask NULL for dense attention), without the
+ * workspace arguments: the scratch the backward needs (fa_bwd_workspace_size
+ * bytes) lives in one device array of 16 MiB inside the library, which each
+ * GPU the library runs on holds until the process ends. Sizes whose
+ * fa_bwd_workspace_size exceeds 16 MiB (about B*H*ceil(N/128)*128 > 2
+ * million rows) return FA_ERR_WORKSPACE before anything is enqueued. The
+ * call makes no hipMalloc, hipFree or other allocation; its first call on a
+ * device looks up that device's array address once. Every call on one GPU
+ * shares that GPU's array, and nothing needs to start at zero (each call
+ * writes the scratch before reading it), but calls that overlap in time on
+ * one GPU (on different streams, or from several host threads without
+ * ordering) race on it and give wrong results. */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, int causal, float scale,
+                   const uint8_t* block_mask, void* stream);
+
 /* One backward kernel alone, so a caller can time or overlap them (the
  * three steps of the backward pass that recomputes attention on chip,
  * Stanford FlashAttention summary, recomputation; the dK/dV and dQ steps

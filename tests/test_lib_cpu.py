@@ -241,3 +241,21 @@ def test_every_declaration_cites_a_passage_or_says_none():
         block = text[text.rfind("/*", 0, pos):text.rfind("*/", 0, pos) + 2]
         flat = " ".join(w for w in block.split() if w != "*")
         assert any(c in flat for c in cites), (name, flat[:200])
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """fa_bwd_noalloc checks its arguments and the scratch limit (16 MiB of
+    workspace) before touching the GPU, so these run without one."""
+    f = _lib.fa_bwd_noalloc
+    ptrs = [FAKE] * 6 + [FAKE] * 3
+    # 2 heads x 4M rows need far more than 16 MiB of workspace
+    assert f(*ptrs, 2, 1, 1 << 22, 64, 0, 0.125, None, None) == -5
+    st, need = _lib.fa_bwd_workspace_size(32, 16, 2048, 128)
+    assert st == 0 and need <= 16 << 20
+    st, need = _lib.fa_bwd_workspace_size(64, 64, 2048, 128)
+    assert st == 0 and need > 16 << 20
+    assert f(*ptrs, 64, 64, 2048, 128, 0, 0.125, None, None) == -5
+    assert f(None, *ptrs[1:], 1, 1, 64, 64, 0, 0.125, None, None) == -1
+    assert f(*ptrs, 1, 1, 64, 96, 0, 0.125, None, None) == -3
+    assert f(*ptrs, 1, 1, 64, 64, 0, -1.0, None, None) == -4
+    assert f(FAKE + 8, *ptrs[1:], 1, 1, 64, 64, 0, 0.125, None, None) == -8
