@@ -42,6 +42,7 @@ METRIC = "attention TFLOPs/s fwd and fwd+bwd (bf16, d=64/128, causal) and % MFMA
 # MI355X: 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU (dense) = the published 2.5 PFLOP/s.
 CUS, SCLK_GHZ, BF16_FLOP_PER_CLK_CU = 256, 2.4, 4096
 PEAK_TFLOPS = CUS * SCLK_GHZ * BF16_FLOP_PER_CLK_CU / 1e3
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 
 WORKLOADS = {
     "causal_b4_h16_n4096_d128_fwdbwd": dict(B=4, H=16, N=4096, d=128, causal=True, sparse=False, bwd=True),
@@ -110,19 +111,143 @@ def source_sha(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None if there is none for this workload or the kernel source changed."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
+# Counter passes (one rocprofv3 --pmc run each; see --summarize-counters).
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+               "SQ_WAVES GRBM_GUI_ACTIVE")
+SIMDS = 4 * CUS  # SIMDs of the chip
+XCDS = 8
+
+
+def load_counters(workload: str, kernel: str):
+    """Counter record of `kernel` (HBM bytes per launch, MFMA busy, ...) from
+    the committed summary, or None if there is none for this workload or the
+    kernel's source changed since the counters were taken."""
     try:
-        with open(path) as f:
+        with open(COUNTERS_JSON) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     rec = data.get(workload, {}).get(kernel)
     if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def _kernel_role(name: str):
+    if "fa_fwd_kernel" in name:
+        return "fwd"
+    if "fa_bwd_pre_kernel" in name:
+        return "bwd_pre"
+    if "fa_bwd_dkdv_kernel" in name:
+        return "bwd_dkdv"
+    if "fa_bwd_dq_kernel" in name:
+        return "bwd_dq"
+    return None
+
+
+def _counter_means(run_dir: str, counters):
+    """Mean value per dispatch of each counter, per kernel name, from the
+    rocprofv3 database(s) under run_dir."""
+    import collections
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True)
+    if len(dbs) != 1:
+        raise SystemExit(f"{run_dir}: expected one rocprofv3 *_results.db, found {len(dbs)}")
+    con = sqlite3.connect(dbs[0])
+    out = collections.defaultdict(dict)
+    for cname in counters:
+        rows = con.execute("select dispatch_id, kernel_name, sum(value) from counters_collection where counter_name=? "
+                           "group by dispatch_id, kernel_name", (cname,)).fetchall()
+        acc = collections.defaultdict(list)
+        for _, kn, v in rows:
+            acc[re.sub(r"\(.*", "", kn).replace("void fa::", "")].append(v)
+        for kn, vals in acc.items():
+            out[kn][cname] = sum(vals) / len(vals)
+    return out
+
+
+def summarize_counters(run_root: str, workload: str) -> int:
+    """Turn the counter runs of one workload into profiles/counters.json and
+    profiles/counters_<workload>.txt. run_root holds one rocprofv3 output
+    directory per pass, each made from the repository root with
+    TMPDIR=/tmp:
+      cal_fetch, cal_write: rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE) -d RUN_ROOT/cal_fetch (cal_write)
+                            -o run -- python3 bench.py --copy-calibration
+      fetch, write:         rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE) -d RUN_ROOT/fetch (write) -o run
+                            -- python3 bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline
+      sq:                   rocprofv3 --pmc <SQ_COUNTERS> -d RUN_ROOT/sq -o run -- python3 bench.py
+                            --workload W --steps 3 --warmup 1 --no-cpu-baseline
+    FETCH_SIZE and WRITE_SIZE are in KiB and are scaled by what they read for
+    a plain 1 GiB device copy (bytes = KiB * 1024 * (2^30 / 1024) / copy's
+    reading). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GRBM_GUI_ACTIVE
+    / XCDs) (GRBM_GUI_ACTIVE sums the XCDs' clocks); resident waves per SIMD =
+    4 * SQ_WAVE_CYCLES / (SIMDs * GRBM_GUI_ACTIVE / XCDs)."""
+    cal = {}
+    for c, sub in (("FETCH_SIZE", "cal_fetch"), ("WRITE_SIZE", "cal_write")):
+        vals = _counter_means(os.path.join(run_root, sub), [c])
+        cal[c] = max(v[c] for v in vals.values())  # the 1 GiB copy kernel
+    ff, wf = (1 << 30) / 1024 / cal["FETCH_SIZE"], (1 << 30) / 1024 / cal["WRITE_SIZE"]
+    fe = _counter_means(os.path.join(run_root, "fetch"), ["FETCH_SIZE"])
+    wr = _counter_means(os.path.join(run_root, "write"), ["WRITE_SIZE"])
+    sq = _counter_means(os.path.join(run_root, "sq"), SQ_COUNTERS.split())
+    recs = {}
+    for kn in sorted(set(fe) | set(sq)):
+        role = _kernel_role(kn)
+        if role is None:
+            continue
+        rec = {"kernel": kn, "source_sha": source_sha(KERNEL_SOURCES[role])}
+        if kn in fe and kn in wr:
+            fb, wb = fe[kn]["FETCH_SIZE"] * 1024 * ff, wr[kn]["WRITE_SIZE"] * 1024 * wf
+            rec.update(fetch_kib_raw=fe[kn]["FETCH_SIZE"], write_kib_raw=wr[kn]["WRITE_SIZE"],
+                       fetch_factor=round(ff, 4), write_factor=round(wf, 4), fetch_bytes=int(fb),
+                       write_bytes=int(wb), bytes_per_launch=int(fb + wb))
+        if kn in sq:
+            v = sq[kn]
+            g = v["GRBM_GUI_ACTIVE"] / XCDS
+            mf = v["SQ_INSTS_MFMA"]
+            rec.update(mfma_busy=round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * g), 4),
+                       waves_per_simd=round(4 * v["SQ_WAVE_CYCLES"] / (SIMDS * g), 3),
+                       valu_per_mfma=round(v["SQ_INSTS_VALU"] / mf, 3) if mf else None,
+                       lds_per_mfma=round(v["SQ_INSTS_LDS"] / mf, 3) if mf else None,
+                       gpu_cycles=round(g), raw_sq={k: v[k] for k in sorted(v)})
+        recs[role] = rec
+    try:
+        with open(COUNTERS_JSON) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = recs
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    cmd = ("rocprofv3 --pmc {c} -d RUN_ROOT/{d} -o run -- python3 bench.py --workload " + workload +
+           " --steps 3 --warmup 1 --no-cpu-baseline")
+    lines = [f"# Counters per launch (mean of the warm-up and timed dispatches), workload {workload}",
+             "# commands (one pass each, from the repository root, TMPDIR=/tmp):",
+             "#   " + cmd.format(c="FETCH_SIZE", d="fetch"), "#   " + cmd.format(c="WRITE_SIZE", d="write"),
+             "#   " + cmd.format(c=SQ_COUNTERS, d="sq"),
+             "#   rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE) -d RUN_ROOT/cal_fetch (cal_write) -o run -- "
+             "python3 bench.py --copy-calibration",
+             f"#   python3 bench.py --summarize-counters RUN_ROOT --workload {workload}",
+             f"# copy calibration: FETCH_SIZE {cal['FETCH_SIZE']:.1f} KiB and WRITE_SIZE {cal['WRITE_SIZE']:.1f} KiB "
+             f"for a 1 GiB copy -> factors {ff:.4f}, {wf:.4f}",
+             "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * GRBM_GUI_ACTIVE / 8)",
+             f"{'kernel':10s} {'fetch_MiB':>10s} {'write_MiB':>10s} {'MFMA_busy':>10s} {'waves/SIMD':>11s} "
+             f"{'VALU/MFMA':>10s} {'LDS/MFMA':>9s}"]
+    for role in ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"):
+        r = recs.get(role)
+        if not r:
+            continue
+        def fm(k, scale=1.0, fmt="{:10.1f}"):
+            return fmt.format(r[k] / scale) if r.get(k) is not None else f"{'-':>10s}"
+        lines.append(f"{role:10s} {fm('fetch_bytes', 2**20)} {fm('write_bytes', 2**20)} "
+                     f"{fm('mfma_busy', 1, '{:10.3f}')} {fm('waves_per_simd', 1, '{:11.2f}')} "
+                     f"{fm('valu_per_mfma', 1, '{:10.2f}')} {fm('lds_per_mfma', 1, '{:9.2f}')}")
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
 
 
 def cpu_threads() -> int:
@@ -211,7 +336,16 @@ def main(argv=None):
                     help="run the forward through fa_fwd_tiles with this tile configuration (tile-size study)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    ap.add_argument("--atomic-rate", action="store_true",
+                    help="only measure the fp32 atomic-add rate in the dQ accumulation layout and the time a "
+                         "dQ-by-atomics backward of --workload would spend on its adds, then exit")
+    ap.add_argument("--summarize-counters", metavar="RUN_ROOT", default=None,
+                    help="turn the rocprofv3 counter runs under RUN_ROOT (for --workload) into "
+                         "profiles/counters.json and profiles/counters_<workload>.txt, then exit (no GPU)")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
@@ -223,6 +357,40 @@ def main(argv=None):
 
     from exact_io_aware_69_amd import _lib
     from synth import make_inputs
+
+    if args.atomic_rate:
+        # fp32 atomic adds in the dQ accumulation layout (fa_atomic_add_probe),
+        # against the adds a dQ-by-atomics backward of --workload would need:
+        # one per (query row, head-dimension element) per visited dK/dV key tile.
+        _lib.lib()
+        cfg = workload_config(args.workload)
+        dst = torch.zeros(4096 * 64 * 128, dtype=torch.float32, device="cuda:0")
+        sptr = torch.cuda.current_stream().cuda_stream
+        wgs, reps = 256 * 8, 64
+        _lib.check(_lib.fa_atomic_add_probe(dst.data_ptr(), dst.numel(), wgs, 2, sptr), "fa_atomic_add_probe")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _lib.check(_lib.fa_atomic_add_probe(dst.data_ptr(), dst.numel(), wgs, reps, sptr), "fa_atomic_add_probe")
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        rate = wgs * 256 * 16 * reps / (ms * 1e-3)
+        st, _, bn = _lib.fa_tile_config(1, cfg["d"], cfg["causal"])
+        _lib.check(st, "fa_tile_config")
+        B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+        nk = -(-N // bn)
+        if cfg["sparse"]:
+            # each kept 128 x 128 mask block: 128 query rows per key tile of the block
+            mask = make_inputs(args.seed, B, H, N, d, with_do=False, sparse=True)["mask"]
+            adds = B * int(mask.astype(bool).sum()) * 128 * d * (128 // bn)
+        else:
+            rows = sum(N - t * bn for t in range(nk)) if cfg["causal"] else nk * N  # query rows per key tile
+            adds = B * H * rows * d
+        print(json.dumps({"atomic_add_rate_per_s": rate, "probe_ms": round(ms, 4), "workload": args.workload,
+                          "dq_atomic_adds": adds, "dq_atomic_ms_at_this_rate": round(adds / rate * 1e3, 4),
+                          "key_tile": bn}))
+        return 0
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -344,11 +512,30 @@ def main(argv=None):
     kern_flops = {"fwd": f_fwd, "bwd_pre": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd, "bwd": 2.5 * f_fwd}
     dom = max(names, key=lambda n: kern_ms[n])
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    # Counter figures (HBM bytes, MFMA busy) come from the committed rocprofv3
+    # summary of the same workload, valid while the kernel source is the one
+    # they were taken on; the GB/s divide those bytes by this run's live
+    # launch time. Counters exist for the default kernels only.
+    default_kernels = not (args.standard or args.fa1 or tiles or drop)
+    counters = {}
+    for n in names:
+        rec = load_counters(args.workload, n) if default_kernels and n in KERNEL_SOURCES else None
+        if rec is None:
+            continue
+        c = {"mfma_busy": rec.get("mfma_busy"), "waves_per_simd": rec.get("waves_per_simd")}
+        if rec.get("bytes_per_launch") is not None:
+            gbps = rec["bytes_per_launch"] / (kern_ms[n] * 1e-3) / 1e9
+            c.update(hbm_bytes=rec["bytes_per_launch"], hbm_gbps=round(gbps, 1),
+                     hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+        counters[n] = c
+    dc = counters.get(dom, {})
     roofline = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-        # counters were taken for the default kernels only
-        "traffic": None if (args.standard or args.fa1 or tiles or drop) else load_traffic(args.workload, dom),
+        "traffic": dc.get("hbm_bytes"),
+        "hbm_gbps": dc.get("hbm_gbps"), "hbm_frac": dc.get("hbm_frac"), "mfma_busy": dc.get("mfma_busy"),
+        "counters_source": ("stored: profiles/counters.json (rocprofv3 --pmc on this kernel source); "
+                            "hbm_gbps = those bytes / this run's launch time") if dc else None,
         "avg_ms": round(kern_ms[dom], 4),
         "flops_per_launch": kern_flops[dom],
     }
@@ -382,6 +569,7 @@ def main(argv=None):
         "peak_tflops": round(PEAK_TFLOPS, 1),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
         "roofline": roofline,
+        "counters": counters or None,
     }
     if std_ws is not None:
         out["workspace_bytes"] = std_ws.numel()

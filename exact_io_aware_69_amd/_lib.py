@@ -47,6 +47,7 @@ SIGNATURES = {
                                  _p, _p, _p]),
     "fa_status_str": (ctypes.c_char_p, [_i]),
     "fa_build_id": (ctypes.c_char_p, []),
+    "fa_atomic_add_probe": (_i, [_p, _sz, _i, _i, _p]),
 }
 
 FA_OK = 0
@@ -192,6 +193,10 @@ def fa_bwd_debug_visits(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, sca
                         workspace_bytes, visited_kv, visited_q, stream):
     return lib().fa_bwd_debug_visits(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, int(causal), scale,
                                      block_mask, workspace, workspace_bytes, visited_kv, visited_q, stream)
+
+
+def fa_atomic_add_probe(dst, dst_floats, workgroups, reps, stream):
+    return lib().fa_atomic_add_probe(dst, dst_floats, workgroups, reps, stream)
 
 
 def fa_build_id() -> str:

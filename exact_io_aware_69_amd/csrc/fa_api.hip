@@ -28,6 +28,7 @@ hipError_t launch_fwd_dropout(const FwdParams& p, int BH, int d, bool causal, bo
 hipError_t launch_bwd_dropout(const BwdParams& p, int BH, int d, bool causal, bool sparse, int stages,
                               hipStream_t st);
 hipError_t launch_dropout_keep(uint8_t* keep, int BH, int N, const Dropout& dr, hipStream_t st);
+hipError_t launch_atomic_probe(float* dst, size_t nblk, int wgs, int reps, hipStream_t st);
 }  // namespace fa
 
 namespace {
@@ -331,6 +332,15 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed, uint32_
   const int st = make_dropout(dropout_p, seed, offset, &dr);
   if (st != FA_OK) return st;
   const hipError_t e = fa::launch_dropout_keep(keep, B * H, N, dr, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_atomic_add_probe(float* dst, size_t dst_floats, int workgroups, int reps, void* stream) {
+  if (!dst) return FA_ERR_NULL;
+  if (!aligned16(dst)) return FA_ERR_ALIGN;
+  const size_t nblk = dst_floats / (64 * 128);
+  if (nblk < 1 || workgroups < 1 || reps < 1) return FA_ERR_SHAPE;
+  const hipError_t e = fa::launch_atomic_probe(dst, nblk, workgroups, reps, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -826,6 +826,30 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ fp32 atomic-add rate
+// The accumulation a dQ-by-atomics backward would make: every wave adds the
+// 16 registers of a 32 x 32 fp32 MFMA result (lanes 0-31 one row, lanes
+// 32-63 the row four below, 32 consecutive floats each) into a [rows][128]
+// fp32 matrix, `reps` times, with global atomic adds (no return). Workgroup
+// b adds into 32 KiB block b % nblk. Measures the rate that decides between
+// atomics and a separate dQ pass.
+__global__ __launch_bounds__(256) void fa_atomic_probe_kernel(float* __restrict__ dst, size_t nblk, int reps) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float* base = dst + (blockIdx.x % nblk) * (64 * 128);
+  for (int it = 0; it < reps; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = (16 * w + 8 * (r / 4) + 4 * (lane / 32) + (r % 4)) % 64;
+      atomicAdd(base + row * 128 + 32 * (it % 4) + (lane & 31), 1.0f);
+    }
+  }
+}
+
+hipError_t launch_atomic_probe(float* dst, size_t nblk, int wgs, int reps, hipStream_t st) {
+  hipLaunchKernelGGL(fa_atomic_probe_kernel, dim3((unsigned)wgs), dim3(256), 0, st, dst, nblk, reps);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launchers
 // stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>

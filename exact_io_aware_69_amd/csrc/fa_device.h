@@ -103,6 +103,16 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nwg) {
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// The value x, opaque to the compiler (an empty asm that claims to rewrite
+// the register; no instruction is emitted). Per-lane LDS offsets computed
+// once and passed through this are added to compile-time stage bases as
+// plain additions, which the compiler folds into the instructions' offset
+// fields instead of materialising one register per (stage, offset) pair.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Byte offset of element (row, col) of a [rows][D] bf16 tile in LDS whose
 // 16-byte chunks are XOR-swizzled per row. The swizzle value runs through
 // all D/8 chunk indices over D/8 consecutive rows (row-wise operand reads by

@@ -278,6 +278,16 @@ int fa_bwd_debug_visits(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes,
                         uint8_t* visited_kv, uint8_t* visited_q, void* stream);
 
+/* Measurement utility, which no passage of the pages defines: the fp32
+ * atomic-add rate of the accumulation a dQ-by-atomics backward would make
+ * (the alternative to a separate dQ pass that the FlashAttention-2 review,
+ * "Proposed method", leaves open). Enqueues one kernel of `workgroups`
+ * workgroups of 256 threads; each adds 1.0f, 16 * 256 * reps times, into
+ * the 32 x 32 MFMA result layout of a [64][128] fp32 block of dst (16-byte
+ * aligned, dst_floats >= 8192 floats, contents overwritten by sums).
+ * Adds = workgroups * 256 * 16 * reps; time it on the stream. */
+int fa_atomic_add_probe(float* dst, size_t dst_floats, int workgroups, int reps, void* stream);
+
 /* Identity of the sources this library was built from: the first 16 hex
  * digits of a SHA-256 over the kernel sources, the headers and the build
  * script, fixed at build time (static string, never NULL). A utility of

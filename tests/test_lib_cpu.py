@@ -259,3 +259,12 @@ def test_noalloc_rejects_before_any_hip_call():
     assert f(*ptrs, 1, 1, 64, 96, 0, 0.125, None, None) == -3
     assert f(*ptrs, 1, 1, 64, 64, 0, -1.0, None, None) == -4
     assert f(FAKE + 8, *ptrs[1:], 1, 1, 64, 64, 0, 0.125, None, None) == -8
+
+
+def test_atomic_probe_rejects_bad_arguments():
+    f = _lib.fa_atomic_add_probe
+    assert f(None, 8192, 1, 1, None) == -1
+    assert f(FAKE + 4, 8192, 1, 1, None) == -8
+    assert f(FAKE, 8191, 1, 1, None) == -2
+    assert f(FAKE, 8192, 0, 1, None) == -2
+    assert f(FAKE, 8192, 1, 0, None) == -2

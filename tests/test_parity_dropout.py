@@ -148,11 +148,12 @@ def test_dropout_parity_peaky_and_blocksparse(causal):
     check_grads((dq, dk, dv), ref)
 
 
-def test_zero_dropout_matches_plain_path():
+@pytest.mark.parametrize("d", [64, 128])
+def test_zero_dropout_matches_plain_path(d):
     """p = 0 keeps everything: results equal the plain kernels' bit for bit
     in O and lse (the same arithmetic with every keep test passing)."""
     from exact_io_aware_69_amd import attention
-    inp = make_inputs(73, 1, 2, 200, 128)
+    inp = make_inputs(73, 1, 2, 200, d)
     q, k, v, o, lse, _ = run_fwd(inp, True, 0.088, 0.0, 5, 0)
     o2, lse2 = attention.forward(q, k, v, causal=True, scale=0.088)
     torch.cuda.synchronize()
