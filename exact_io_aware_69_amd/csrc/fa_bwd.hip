@@ -314,6 +314,21 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   const int trow = 4 * hh + (jj >> 2);
   const int tcol = 16 * (g & 1) + 4 * (jj & 3);
   const int arow = lane & 31;
+  // Per-lane LDS offsets, computed once and opaque to the compiler, so that
+  // every stage and block base (compile-time constants) folds into the
+  // instructions' offset fields: the row read of k-step kk (32-row blocks and
+  // 16-row k-steps differ by constants, the swizzle repeating every 16 rows),
+  // the two transposing reads (rows +0 and +8) of 32-column block dt, this
+  // lane's 16-byte slot in the P exchange and its f32x4 of lse / -D rows.
+  uint32_t rofs[D / 16], tofs[2][D / 32];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) rofs[kk] = opaque(tile_off<D>(arow, 16 * kk + 8 * hh));
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) tofs[pt][dt] = opaque(tile_off<D>(trow + 8 * pt, 32 * dt + tcol));
+  const uint32_t pofs = opaque(lane * 16);
+  const uint32_t lofs = opaque(16 * hh);
 
   f32x16 sd[QB];       // S (P-wave) or dP - D (dS-wave) of the current tile
   bf16x8 pend[QB][2];  // P (P-wave) or dS (dS-wave) of the previous tile, B operand of its deferred product
@@ -329,10 +344,10 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (DSW) {
-        const FA_LDS float* dl = sb.l + LROW;
+        const FA_LDS uint8_t* dl = reinterpret_cast<const FA_LDS uint8_t*>(sb.l + LROW);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 4 * (32 * qb + 8 * rg) + lofs);
 #pragma unroll
           for (int e = 0; e < 4; ++e) sd[qb][4 * rg + e] = d4[e];
         }
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        sd[qb] = mfma32(ld_lds16(a1, tile_off<D>(32 * qb + arow, 16 * kk + 8 * hh)), kvf[kk], sd[qb]);
+        sd[qb] = mfma32(ld_lds16(a1 + 32 * qb * D * 2, rofs[kk]), kvf[kk], sd[qb]);
     // Issue order: the -D rows and the operands of the first two k-steps,
     // then each k-step's products followed by the reads two k-steps ahead.
     __builtin_amdgcn_sched_group_barrier(0x100, (DSW ? 4 * QB : 0) + 2 * QB, 0);
@@ -384,13 +399,12 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int rr = 32 * qb + 16 * ks + trow;
-          const int cc = 32 * kg + tcol;
-          const bf16x8 aT = join_tr(ld_lds_tr(a2, tile_off<D>(rr, cc)), ld_lds_tr(a2, tile_off<D>(rr + 8, cc)));
+          const FA_LDS uint8_t* a2r = a2 + (32 * qb + 16 * ks) * D * 2;
+          const bf16x8 aT = join_tr(ld_lds_tr(a2r, tofs[0][kg]), ld_lds_tr(a2r, tofs[1][kg]));
 #pragma unroll
           for (int g2 = 0; g2 < KG; ++g2) {
             const bf16x8 pb =
-                *reinterpret_cast<const FA_LDS bf16x8*>(sb.px + (g2 * QB + qb) * 2048 + ks * 1024 + lane * 16);
+                *reinterpret_cast<const FA_LDS bf16x8*>(sb.px + (g2 * QB + qb) * 2048 + ks * 1024 + pofs);
             acc[g2] = mfma32(aT, pb, acc[g2]);
           }
         }
@@ -423,9 +437,8 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const int rr = 32 * qb + 16 * ks + trow;
-          const int cc = 32 * dt + tcol;
-          const bf16x8 aT = join_tr(ld_lds_tr(a2, tile_off<D>(rr, cc)), ld_lds_tr(a2, tile_off<D>(rr + 8, cc)));
+          const FA_LDS uint8_t* a2r = a2 + (32 * qb + 16 * ks) * D * 2;
+          const bf16x8 aT = join_tr(ld_lds_tr(a2r, tofs[0][dt]), ld_lds_tr(a2r, tofs[1][dt]));
           acc[dt] = mfma32(aT, pend[qb][ks], acc[dt]);
         }
     // Issue order: the reads of the first four products, then each product
@@ -445,17 +458,17 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   // where it is dropped in the copy for the partner (so the keep bit travels
   // with it), and the dV operand is P on kept entries, 0 elsewhere.
   auto exp_p = [&](int i, const Stage& sb, bf16x8 (&pnew)[QB][2]) __attribute__((always_inline)) {
-    const FA_LDS float* ls = sb.l;
+    const FA_LDS uint8_t* ls = reinterpret_cast<const FA_LDS uint8_t*>(sb.l);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float pe[16];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 32 * qb + 8 * rg + 4 * hh);
+        const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>(ls + 4 * (32 * qb + 8 * rg) + lofs);
 #pragma unroll
         for (int e = 0; e < 4; ++e) pe[4 * rg + e] = fast_exp2(fmaf(sd[qb][4 * rg + e], c, -l4[e]));
       }
-      FA_LDS uint8_t* dst = sb.px + (kg * QB + qb) * 2048 + lane * 16;
+      FA_LDS uint8_t* dst = sb.px + (kg * QB + qb) * 2048 + pofs;
       if (DROP) {
         // Values 4*rg .. 4*rg+3 are queries i0 .. i0+3 at this lane's key.
         // The quad of lanes holding keys 4m .. 4m+3 makes the four
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
     bf16x8 pp[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const FA_LDS uint8_t* src = sb.px + (kg * QB + qb) * 2048 + lane * 16;
+      const FA_LDS uint8_t* src = sb.px + (kg * QB + qb) * 2048 + pofs;
       pp[qb][0] = *reinterpret_cast<const FA_LDS bf16x8*>(src);
       pp[qb][1] = *reinterpret_cast<const FA_LDS bf16x8*>(src + 1024);
     }
@@ -506,10 +519,10 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       if (DROP) {
         // Kept (P >= 0): dS = P (dP - D) with dP, D both in units of
         // 1 - p; dropped (P stored negated): dS = -P D = P' * D.
-        const FA_LDS float* dl = sb.l + LROW;
+        const FA_LDS uint8_t* dl = reinterpret_cast<const FA_LDS uint8_t*>(sb.l + LROW);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 32 * qb + 8 * rg + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>(dl + 4 * (32 * qb + 8 * rg) + lofs);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rg + e;
@@ -547,7 +560,8 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
     };
     // One step: tile ic in stage SC; the previous tile is in stage SP, the
     // next one is copied into stage SN. Returns false after the last tile.
-    auto step = [&](int SC) __attribute__((always_inline)) -> bool {
+    auto step = [&](auto scur) __attribute__((always_inline)) -> bool {
+      const int SC = scur;  // a compile-time constant in the unrolled loop
       const int SP = SC == 0 ? 2 : SC - 1, SN = SC == 2 ? 0 : SC + 1;
       const int in = next_tile(ic + 1);
       if (!DSW && in < n_qt) dma_q(in, stage(SN));
@@ -575,9 +589,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       wait_vmem();
       __syncthreads();
       ic = in;
-      if (ic < n_qt) return true;
-      tail(SC);
-      return false;
+      return ic < n_qt;
     };
     // First tile (stage 0): its row products and P only.
     if (!DSW) dma_q(ic, stage(0));
@@ -597,8 +609,25 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       tail(0);
       return;
     }
-    int sc = 1;
-    while (step(sc)) sc = sc == 2 ? 0 : sc + 1;
+    // Stages rotate 1, 2, 0, 1, ...; the last tile's transposed products
+    // (tail) use the stage it was in. Without dropout the loop is unrolled
+    // by three, so that every stage index is a compile-time constant and each
+    // LDS address a per-lane register plus an immediate; the dropout kernels
+    // need those registers for the generator and keep the run-time index.
+    int last = 1;
+    if constexpr (DROP) {
+      while (step(last)) last = last == 2 ? 0 : last + 1;
+    } else {
+      for (;;) {
+        if (!step(std::integral_constant<int, 1>())) break;
+        last = 2;
+        if (!step(std::integral_constant<int, 2>())) break;
+        last = 0;
+        if (!step(std::integral_constant<int, 0>())) break;
+        last = 1;
+      }
+    }
+    tail(last);
   };
   if (dswave)
     sweep(std::true_type());
@@ -711,12 +740,26 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   };
 
   const float c = p.c;
-
-  auto tile = [&](int j, const FA_LDS uint8_t* ks, const FA_LDS uint8_t* vs, bool need_mask)
-                  __attribute__((always_inline)) {
+  // Per-lane LDS offsets, computed once and opaque to the compiler (stage and
+  // block bases are compile-time constants that fold into the instructions'
+  // offset fields): the K / V row read of k-step kk (32-row blocks differ by
+  // a constant) and the two transposing reads of Kᵀ (rows +0 and +8 of a
+  // 16-key k-step) for 32-column block dt.
+  uint32_t rofs[D / 16], tofs[2][D / 32];
+  {
     const int g = lane >> 4, jj = lane & 15;
     const int trow = 4 * h2 + (jj >> 2);
     const int tcol = 16 * (g & 1) + 4 * (jj & 3);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) rofs[kk] = opaque(tile_off<D>(lane & 31, 16 * kk + 8 * h2));
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) tofs[pt][dt] = opaque(tile_off<D>(trow + 8 * pt, 32 * dt + tcol));
+  }
+
+  auto tile = [&](int j, const FA_LDS uint8_t* ks, const FA_LDS uint8_t* vs, bool need_mask)
+                  __attribute__((always_inline)) {
     const int kbase = j * BN;
     f32x16 s[NS], dp[NS];
 #pragma unroll
@@ -732,9 +775,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int mt = 0; mt < NS; ++mt) {
-        const int row = 32 * mt + (lane & 31);
-        s[mt] = mfma32(ld_lds16(ks, tile_off<D>(row, 16 * kk + 8 * h2)), qf[kk], s[mt]);
-        dp[mt] = mfma32(ld_lds16(vs, tile_off<D>(row, 16 * kk + 8 * h2)), dof[kk], dp[mt]);
+        s[mt] = mfma32(ld_lds16(ks + 32 * mt * D * 2, rofs[kk]), qf[kk], s[mt]);
+        dp[mt] = mfma32(ld_lds16(vs + 32 * mt * D * 2, rofs[kk]), dof[kk], dp[mt]);
       }
     // Value r of block mt is key kbase + 32*mt + 8*(r/4) + 4*h2 + r%4; it is
     // visible iff key <= min(N - 1, qi) (causal) or key <= N - 1.
@@ -773,9 +815,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int rr = 16 * kk + trow;
-        const int cc = 32 * dt + tcol;
-        const bf16x8 kT = join_tr(ld_lds_tr(ks, tile_off<D>(rr, cc)), ld_lds_tr(ks, tile_off<D>(rr + 8, cc)));
+        const FA_LDS uint8_t* kr = ks + 16 * kk * D * 2;
+        const bf16x8 kT = join_tr(ld_lds_tr(kr, tofs[0][dt]), ld_lds_tr(kr, tofs[1][dt]));
         dqt[dt] = mfma32(kT, dsb, dqt[dt]);
       }
       // No scheduling fence between k-steps: the next k-step's transposing
