@@ -128,6 +128,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
     cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
   };
 
+  // Per-lane LDS offsets, computed once and opaque to the compiler, so that
+  // the stage bases (compile-time constants) and the 32-key block and k-step
+  // offsets fold into the instructions' offset fields: the K row of k-step
+  // kk, and the two transposing reads of V^T (rows +0 and +8 of a 16-key
+  // k-step; the swizzle repeats every 16 rows) for 32-column block dt.
+  uint32_t kofs[D / 16], vofs[2][D / 32];
+  {
+    const int g = (lane >> 4) & 1, jj = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kofs[kk] = opaque(tile_off<D>(lane & 31, 16 * kk + 8 * h2));
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        vofs[pt][dt] = opaque(tile_off<D>(4 * h2 + (jj >> 2) + 8 * pt, 32 * dt + 16 * g + 4 * (jj & 3)));
+  }
+
   // S^T tile = K_j Q^T from an LDS stage.
   auto scores = [&](const FA_LDS uint8_t* ks, f32x16 (&s)[NS]) __attribute__((always_inline)) {
 #pragma unroll
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int mt = 0; mt < NS; ++mt)
-        s[mt] = mfma32(ld_lds16(ks, tile_off<D>(32 * mt + (lane & 31), 16 * kk + 8 * h2)), qf[kk], s[mt]);
+        s[mt] = mfma32(ld_lds16(ks + 32 * mt * D * 2, kofs[kk]), qf[kk], s[mt]);
     // Issue order: the K reads of the first two k-steps, then each k-step's
     // products followed by the reads two k-steps ahead.
     if constexpr (AHEAD) {
@@ -162,9 +179,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   const float c = p.c;
-  const int g = lane >> 4, jj = lane & 15;
-  const int vrow = 4 * h2 + (jj >> 2);
-  const int vcol = 16 * (g & 1) + 4 * (jj & 3);
 
   // Online softmax of one score tile and O^T += V^T P^T.
   auto softmax_pv = [&](f32x16 (&s)[NS], int j, const FA_LDS uint8_t* vs, bool need_mask)
@@ -218,8 +232,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
     auto read_vt = [&](int kk, bf16x8 (&vT)[D / 32]) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        vT[dt] = join_tr(ld_lds_tr(vs, tile_off<D>(16 * kk + vrow, 32 * dt + vcol)),
-                         ld_lds_tr(vs, tile_off<D>(16 * kk + 8 + vrow, 32 * dt + vcol)));
+        vT[dt] = join_tr(ld_lds_tr(vs + 16 * kk * D * 2, vofs[0][dt]), ld_lds_tr(vs + 16 * kk * D * 2, vofs[1][dt]));
     };
     bf16x8 vnext[D / 32];
     if constexpr (AHEAD) {
