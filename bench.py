@@ -81,7 +81,7 @@ def _workload_arg(name: str) -> str:
     return name
 
 KERNEL_SOURCES = {
-    "fwd": "fa_fwd.hip", "bwd_pre": "fa_bwd.hip", "bwd_dkdv": "fa_bwd.hip", "bwd_dq": "fa_bwd.hip",
+    "fwd": "fa_fwd.hip", "bwd_sched": "fa_bwd.hip", "bwd_dq": "fa_bwd.hip", "bwd_dkdv": "fa_bwd.hip",
 }
 
 
@@ -137,8 +137,8 @@ def load_counters(workload: str, kernel: str):
 def _kernel_role(name: str):
     if "fa_fwd_kernel" in name:
         return "fwd"
-    if "fa_bwd_pre_kernel" in name:
-        return "bwd_pre"
+    if "fa_bwd_sched_kernel" in name:
+        return "bwd_sched"
     if "fa_bwd_dkdv_kernel" in name:
         return "bwd_dkdv"
     if "fa_bwd_dq_kernel" in name:
@@ -235,7 +235,7 @@ def summarize_counters(run_root: str, workload: str) -> int:
              "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * GRBM_GUI_ACTIVE / 8)",
              f"{'kernel':10s} {'fetch_MiB':>10s} {'write_MiB':>10s} {'MFMA_busy':>10s} {'waves/SIMD':>11s} "
              f"{'VALU/MFMA':>10s} {'LDS/MFMA':>9s}"]
-    for role in ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"):
+    for role in ("fwd", "bwd_sched", "bwd_dq", "bwd_dkdv"):
         r = recs.get(role)
         if not r:
             continue
@@ -446,7 +446,11 @@ def main(argv=None):
     if drop:
         names = ["fwd"] + (["bwd"] if cfg["bwd"] else [])
     else:
-        names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if cfg["bwd"] else [])
+        # Backward stages: 0 = block-sparse schedule (enqueues nothing without
+        # a mask, so it is neither called nor timed then), 1 = dQ and the
+        # per-row terms, 2 = dK/dV.
+        bwd_stages = ([0] if mptr is not None else []) + [1, 2]
+        names = ["fwd"] + ([("bwd_sched", "bwd_dq", "bwd_dkdv")[s] for s in bwd_stages] if cfg["bwd"] else [])
 
     def step(events=None):
         if events is not None:
@@ -481,13 +485,13 @@ def main(argv=None):
             if events is not None:
                 events[2].record(stream)
         elif cfg["bwd"]:
-            for stage in range(3):
+            for i, stage in enumerate(bwd_stages):
                 st = _lib.fa_bwd_stage(stage, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        B, H, N, d, causal, scale, mptr, ws.data_ptr(), ws_bytes, sptr)
                 _lib.check(st, "fa_bwd_stage")
                 if events is not None:
-                    events[2 + stage].record(stream)
+                    events[2 + i].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -509,7 +513,7 @@ def main(argv=None):
     # Algorithmic FLOPs attributed to each kernel: the forward's two GEMMs;
     # the dK/dV kernel's four of the backward's five GEMMs (S, dP, dV, dK);
     # the dQ kernel's dQ GEMM (its S and dP recomputation is not counted).
-    kern_flops = {"fwd": f_fwd, "bwd_pre": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd, "bwd": 2.5 * f_fwd}
+    kern_flops = {"fwd": f_fwd, "bwd_sched": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd, "bwd": 2.5 * f_fwd}
     dom = max(names, key=lambda n: kern_ms[n])
     achieved = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     # Counter figures (HBM bytes, MFMA busy) come from the committed rocprofv3

@@ -7,17 +7,21 @@
 // With P = exp(S - lse) recomputed per tile, the gradient is
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_k dO_ik O_ik,
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
-// Three kernels, enqueued in order on one stream:
-//   1. fa_bwd_pre_kernel   per row: -D = -rowsum(dO o O) and lse * log2(e)
-//                          into the workspace, whose rows are padded per head
-//                          to a multiple of 128 (padding: -D = 0, lse = +inf,
-//                          so a padded or fully masked row has P = 0 without
-//                          any test in the hot loops);
+// Two kernels, enqueued in order on one stream (three with a block mask):
+//   0. fa_bwd_sched_kernel block-sparse only: one workgroup per head ranks
+//                          the key and query tiles by falling work;
+//   1. fa_bwd_dq_kernel    one workgroup per (batch, head, 128-query tile),
+//                          streaming 64-row key tiles (recomputes S and dP);
+//                          it also forms each row's -D = -rowsum(dO o O) and
+//                          lse * log2(e) and writes them to the workspace,
+//                          whose rows are padded per head to a multiple of
+//                          128 (padding: -D = 0, lse = +inf, so a padded or
+//                          fully masked row has P = 0 without any test in
+//                          the hot loops);
 //   2. fa_bwd_dkdv_kernel  one workgroup per (batch, head, 128-key tile),
-//                          streaming 64-row query tiles; dK, dV stay in
-//                          registers for the whole sweep;
-//   3. fa_bwd_dq_kernel    one workgroup per (batch, head, 128-query tile),
-//                          streaming 64-row key tiles (recomputes S and dP).
+//                          streaming 64-row query tiles and reading -D and
+//                          lse * log2(e) from the workspace; dK, dV stay in
+//                          registers for the whole sweep.
 // dQ is not accumulated with atomics: fp32 global atomics run at a fraction
 // of the plain store rate on this GPU, and the separate pass keeps every
 // output written once, so results are deterministic.
@@ -35,15 +39,8 @@
 
 namespace fa {
 
-// ------------------------------------------------------------------ -D = -rowsum(dO o O), lse * log2(e)
-// Rows per thread of the preprocess: every thread issues the loads of all
-// its rows before using any, so enough bytes are in flight to stream O and dO
-// at close to the HBM rate.
-constexpr int PRE_ROWS = 4;
-
 // ------------------------------------------------------------------ block-sparse schedule
-// One workgroup per head (run by the first H workgroups of the preprocess
-// launch, alongside its rows): the work of each key tile (mask blocks of its
+// One workgroup per head: the work of each key tile (mask blocks of its
 // column that some query sees) and of each query tile (blocks of its row),
 // then a stable ranking by falling work, so that the dK/dV and dQ launches
 // start their longest tiles first (the tail of a launch is then made of
@@ -130,65 +127,11 @@ struct SchedArgs {
   const uint8_t* mask;
   int* korder;
   int* qorder;
-  int nb, tpb, causal, heads;  // heads = workgroups that build the schedule (one per head)
+  int nb, tpb, causal;
 };
 
-template <int D, bool SCHED>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ dO,
-                                                         const float* __restrict__ lse,
-                                                         float* __restrict__ Dneg, float* __restrict__ lse2,
-                                                         int N, int Npad, size_t rows_pad, float dfac,
-                                                         const SchedArgs sa) {
-  if (SCHED) {
-    // Block-sparse: the first sa.heads workgroups build the schedule, the
-    // rest run the preprocess rows.
-    if ((int)blockIdx.x < sa.heads) {
-      bwd_sched_head(sa.mask, sa.korder, sa.qorder, sa.nb, sa.tpb, sa.causal, (int)blockIdx.x);
-      return;
-    }
-  }
-  const unsigned bid = SCHED ? blockIdx.x - (unsigned)sa.heads : blockIdx.x;
-  constexpr int CH = D / 8;      // lanes per row, 8 elements each
-  constexpr int RPB = 256 / CH;  // rows per workgroup and pass
-  const int c = threadIdx.x % CH;
-  size_t prow[PRE_ROWS], row[PRE_ROWS];
-  bool real[PRE_ROWS];
-  u32x4 a[PRE_ROWS], b[PRE_ROWS];
-#pragma unroll
-  for (int i = 0; i < PRE_ROWS; ++i) {
-    prow[i] = (size_t)bid * (RPB * PRE_ROWS) + (size_t)i * RPB + threadIdx.x / CH;
-    const size_t bh = prow[i] / Npad;
-    const int r = (int)(prow[i] - bh * Npad);
-    real[i] = prow[i] < rows_pad && r < N;
-    row[i] = bh * N + r;
-    a[i] = u32x4{0, 0, 0, 0};
-    b[i] = u32x4{0, 0, 0, 0};
-    if (real[i]) {
-      a[i] = ld_global16(o + row[i] * D + 8 * c);
-      b[i] = ld_global16(dO + row[i] * D + 8 * c);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PRE_ROWS; ++i) {
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(a[i][e] << 16), __uint_as_float(b[i][e] << 16), acc);
-      acc = fmaf(__uint_as_float(a[i][e] & 0xFFFF0000u), __uint_as_float(b[i][e] & 0xFFFF0000u), acc);
-    }
-#pragma unroll
-    for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (prow[i] < rows_pad && c == 0) {
-      float l2 = INFINITY;
-      if (real[i]) {
-        const float l = lse[row[i]];
-        l2 = l == -INFINITY ? INFINITY : l * kLog2e;
-      }
-      Dneg[prow[i]] = -acc * dfac;
-      lse2[prow[i]] = l2;
-    }
-  }
+__global__ __launch_bounds__(256) void fa_bwd_sched_kernel(const SchedArgs sa) {
+  bwd_sched_head(sa.mask, sa.korder, sa.qorder, sa.nb, sa.tpb, sa.causal, (int)blockIdx.x);
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -712,18 +655,42 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BN <= q0 + 31; };
 
   // Q^T and dO^T fragments (B operands, lane = query). Queries past N load a
-  // copy of row N-1; their lse is +inf in the padded workspace, so P = 0.
+  // copy of row N-1; their lse * log2(e) is +inf, so P = 0.
   bf16x8 qf[D / 16], dof[D / 16];
+  float Dq, lse2;  // -D and lse * log2(e) of this lane's query
   {
     const size_t qr = (size_t)min(qi, N - 1) * D + 8 * h2;
+    u32x4 of[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.q + head + qr + 16 * kk));
       dof[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.dO + head + qr + 16 * kk));
+      of[kk] = ld_global16(p.o + head + qr + 16 * kk);
+    }
+    const float l = qi < N ? p.lse[(size_t)bh * N + qi] : -INFINITY;
+    // D = rowsum(dO o O): this lane holds half of its row's elements, the
+    // lane 32 apart the other half. With dropout dP is kept in units of
+    // 1 - p, and so is D.
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 dw = __builtin_bit_cast(u32x4, dof[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__uint_as_float(of[kk][e] << 16), __uint_as_float(dw[e] << 16), acc);
+        acc = fmaf(__uint_as_float(of[kk][e] & 0xFFFF0000u), __uint_as_float(dw[e] & 0xFFFF0000u), acc);
+      }
+    }
+    acc = xhalf_sum(acc);
+    Dq = qi < N ? -acc * p.dfac : 0.f;
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    // The dK/dV pass reads both from the workspace, padded to whole query
+    // tiles per head (rows past N: -D = 0, lse * log2(e) = +inf).
+    if (h2 == 0) {
+      p.Dneg[(size_t)bh * p.Npad + qi] = Dq;
+      p.lse2[(size_t)bh * p.Npad + qi] = lse2;
     }
   }
-  const float lse2 = p.lse2[(size_t)bh * p.Npad + qi];
-  const float Dq = p.Dneg[(size_t)bh * p.Npad + qi];  // -D of this lane's query
   f32x16 dqt[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -892,16 +859,15 @@ hipError_t launch_atomic_probe(float* dst, size_t nblk, int wgs, int reps, hipSt
 }
 
 // ------------------------------------------------------------------ launchers
-// stages: bit 0 = preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel.
+// stages: bit 0 = block-sparse schedule (nothing without a mask), bit 1 =
+// dQ kernel (also writes -D and lse * log2(e) per row to the workspace),
+// bit 2 = dK/dV kernel (reads them). Enqueued in that order.
 template <int D, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
 hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) {
-  if (stages & 1) {
-    const size_t rows_pad = (size_t)BH * p.Npad;
-    constexpr int RPB = 256 / (D / 8) * PRE_ROWS;  // rows per workgroup
-    const unsigned pre_wgs = (unsigned)((rows_pad + RPB - 1) / RPB);
-    const SchedArgs sa{p.mask, p.korder, p.qorder, p.nb, MASK_BLOCK / bwd_kv_bn<D>(), (int)CAUSAL, SPARSE ? p.H : 0};
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D, SPARSE>), dim3(pre_wgs + (unsigned)sa.heads), dim3(256), 0, st, p.o,
-                       p.dO, p.lse, p.Dneg, p.lse2, p.N, p.Npad, rows_pad, p.dfac, sa);
+  static_assert(BWD_Q_BM == BWD_PAD_ROWS, "dQ tiles cover the padded workspace rows exactly");
+  if (SPARSE && (stages & 1)) {
+    const SchedArgs sa{p.mask, p.korder, p.qorder, p.nb, MASK_BLOCK / bwd_kv_bn<D>(), (int)CAUSAL};
+    hipLaunchKernelGGL(fa_bwd_sched_kernel, dim3((unsigned)p.H), dim3(256), 0, st, sa);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -909,6 +875,16 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
   // block-sparse ones, whose tiles the schedule orders by falling work.
   constexpr bool INTERLEAVE = CAUSAL || SPARSE;
   if (stages & 2) {
+    const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
+    const auto kernel = fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
+    static const int wgs = wgs_per_cu((const void*)kernel, 256);
+    BwdParams q = p;
+    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, n_qt2) : 1;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 4) {
     const int n_kt1 = (p.N + bwd_kv_bn<D>() - 1) / bwd_kv_bn<D>();
     // Block-sparse: one slot per (mask block, key tile of the block).
     const int slots = SPARSE ? p.nb * (MASK_BLOCK / bwd_kv_bn<D>()) : n_kt1;
@@ -917,16 +893,6 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
     BwdParams q = p;
     q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, slots) : 1;
     hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * slots)), dim3(64 * bwd_kv_waves<D>()), 0, st, q);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stages & 4) {
-    const int n_qt2 = (p.N + BWD_Q_BM - 1) / BWD_Q_BM;
-    const auto kernel = fa_bwd_dq_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
-    static const int wgs = wgs_per_cu((const void*)kernel, 256);
-    BwdParams q = p;
-    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, n_qt2) : 1;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * n_qt2)), dim3(256), 0, st, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

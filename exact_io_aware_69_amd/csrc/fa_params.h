@@ -85,7 +85,7 @@ struct BwdParams {
   float dfac;   // factor on -D in the workspace: 1, or 1 - p with dropout
   Dropout drop;  // used by the dropout instantiations only
   int hgrp;      // heads per dispatch group (head_rank_order), set per launch
-  // Block-sparse schedule in the workspace (written by the preprocess stage):
+  // Block-sparse schedule in the workspace (written by the schedule stage):
   // per head, the key tiles (korder, SPARSE_KSLOTS(nb) entries) and the
   // query tiles (qorder, nb entries) in order of falling work.
   int* korder;

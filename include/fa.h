@@ -142,7 +142,7 @@ int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
  * float32 D = rowsum(dO * O) and lse * log2(e) for every row
  * (rows padded to 128 per head), then, for block-sparse calls, a schedule of
  * three int32 per (head, 128-row mask block): the key and query tiles of
- * each head in order of falling work, which the preprocess stage writes
+ * each head in order of falling work, which the schedule stage writes
  * (masks of more than 2048 blocks per row keep the plain order). The order
  * changes only which tiles run first, never the results. */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
@@ -150,9 +150,10 @@ int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 /* Backward. Inputs: q, k, v, the forward's o and lse, and the upstream
  * gradient dO. Writes dq, dk, dv (bf16, [B][H][N][d]). Attention
  * probabilities are recomputed on chip from lse (Stanford FlashAttention
- * summary, recomputation in the backward pass). Three kernels on `stream`:
- * D = rowsum(dO*O) into the workspace; dK/dV parallel over key tiles;
- * dQ parallel over query tiles. Deterministic (no atomics). */
+ * summary, recomputation in the backward pass). Two kernels on `stream`:
+ * dQ parallel over query tiles, which also writes D = rowsum(dO*O) and
+ * lse * log2(e) per row into the workspace; then dK/dV parallel over key
+ * tiles, which reads them. Deterministic (no atomics). */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, int causal, float scale,
@@ -193,11 +194,13 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * are parallel over sequence length, FlashAttention-2 review, "Proposed
  * method"); fa_bwd
  * (fa_bwd_blocksparse when block_mask != NULL) is exactly stages 0, 1, 2
- * enqueued in that order on one stream. stage 0: D = rowsum(dO * O) into
- * the workspace (reads o, dO); stage 1: dK and dV (reads q, k, v, lse, dO
- * and the workspace written by stage 0); stage 2: dQ (same inputs). Every
- * pointer argument is validated as in fa_bwd whatever the stage. A stage
- * outside 0..2 returns FA_ERR_SHAPE. */
+ * enqueued in that order on one stream. stage 0: with a block mask, the
+ * schedule of tiles by falling work into the workspace (reads block_mask);
+ * without one it enqueues nothing. stage 1: dQ, and D = rowsum(dO * O) and
+ * lse * log2(e) per row into the workspace (reads q, k, v, o, lse, dO and
+ * the schedule). stage 2: dK and dV (reads q, k, v, dO and the workspace
+ * written by stages 0 and 1). Every pointer argument is validated as in
+ * fa_bwd whatever the stage. A stage outside 0..2 returns FA_ERR_SHAPE. */
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  int B, int H, int N, int d, int causal, float scale,

@@ -1,6 +1,6 @@
 """GPU: a block-sparse mask with more blocks per row than the backward ranks.
 
-The backward's preprocess ranks the mask blocks of a head by work only up
+The backward's schedule stage ranks the mask blocks of a head by work only up
 to 2048 blocks per row; beyond that the dK/dV and dQ launches take their
 tiles in plain order. N = 2049 * 128 = 262272 (nb = 2049) checks that path
 and the kernels' mask windows at their largest (33 windows of 64 blocks per

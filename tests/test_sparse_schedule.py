@@ -1,6 +1,6 @@
-"""GPU: the block-sparse backward schedule that the preprocess stage writes.
+"""GPU: the block-sparse backward schedule that the schedule stage writes.
 
-For a block-sparse backward the preprocess launch also ranks, per head, the
+For a block-sparse backward the schedule launch (stage 0) ranks, per head, the
 key blocks and the query blocks by the number of mask blocks of their column
 (row) that some query sees, falling, ties by index, and stores the order in
 the backward workspace after D and lse * log2(e): three int32 per (head,
