@@ -492,10 +492,10 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
   // The whole sweep, instantiated once per role so that each role's
   // loop-invariant addresses stay in its own branch. Both roles pass the
   // same number of barriers.
-  auto sweep = [&](auto role) __attribute__((always_inline)) {
+  auto sweep = [&](auto role) __attribute__((always_inline)) -> int {
     constexpr bool DSW = decltype(role)::value;
     int ic = next_tile(it_begin);
-    if (ic >= n_qt) return;
+    if (ic >= n_qt) return 0;
     // The last tile's transposed products (its rows are in stage s).
     auto tail = [&](int s) __attribute__((always_inline)) {
       if (DSW) form_ds(stage(s));
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
     ic = in;
     if (ic >= n_qt) {
       tail(0);
-      return;
+      return 0;
     }
     // Stages rotate 1, 2, 0, 1, ...; the last tile's transposed products
     // (tail) use the stage it was in. Without dropout the loop is unrolled
@@ -571,38 +571,31 @@ __global__ __launch_bounds__(bwd_kv_waves<D>() * 64, bwd_kv_waves<D>() == 8 ? 1 
       }
     }
     tail(last);
+    return last;
   };
-  if (dswave)
-    sweep(std::true_type());
-  else
-    sweep(std::false_type());
+  // LDS stage of the last tile (0 without tiles). The other two stages are
+  // free from here on: every wave passed the barrier after their last
+  // reads, and no copy targets them.
+  const int last = dswave ? sweep(std::true_type()) : sweep(std::false_type());
 
+  // dK / dV go out through this wave's slice of the free stages (Q and dO
+  // tile buffers of the two stages other than `last`).
+  constexpr int SLICE = 32 * D * 2;
+  constexpr int PER = TILEB / SLICE;  // slices per tile buffer
+  static_assert(PER >= 1 && 4 * PER >= 2 * KG, "the free stages hold one slice per wave");
+  const int bi = w / PER, f0 = last == 2 ? 0 : last + 1, f1 = last == 0 ? 2 : last - 1;
+  FA_LDS uint8_t* const slice =
+      (bi < 2 ? (FA_LDS uint8_t*)q_raw : (FA_LDS uint8_t*)o_raw) + ((bi & 1) ? f1 : f0) * TILEB + (w % PER) * SLICE;
   if (DV_BY_D && !dswave) {
     // dV of head-dimension block kg for the keys of every key group.
-#pragma unroll
-    for (int g2 = 0; g2 < KG; ++g2) {
-      const int key2 = kb + 32 * g2 + (lane & 31);
-      if (key2 < N) {
-        uint16_t* dst = p.dv + head + (size_t)key2 * D;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d0 = 32 * kg + 8 * rg + 4 * h2;
-          *reinterpret_cast<u32x2*>(dst + d0) =
-              pack4_bf16(acc[g2][4 * rg], acc[g2][4 * rg + 1], acc[g2][4 * rg + 2], acc[g2][4 * rg + 3]);
-        }
-      }
-    }
-  } else if (key < N) {
-    uint16_t* dst = (dswave ? p.dk : p.dv) + head + (size_t)key * D;
+    uint16_t* const vbase = p.dv + head + (size_t)kb * D + 32 * kg;
+    store_tile<KG, true, SLICE>(acc, 1.0f, slice, lane, N - kb,
+                                [&](int r) __attribute__((always_inline)) { return vbase + (size_t)r * D; });
+  } else {
+    uint16_t* const base = (dswave ? p.dk : p.dv) + head + (size_t)k0w * D;
     const float sc = (dswave ? p.scale : 1.0f) * (DROP ? p.drop.scale : 1.0f);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * dt + 8 * rg + 4 * h2;
-        *reinterpret_cast<u32x2*>(dst + d0) = pack4_bf16(acc[dt][4 * rg] * sc, acc[dt][4 * rg + 1] * sc,
-                                                         acc[dt][4 * rg + 2] * sc, acc[dt][4 * rg + 3] * sc);
-      }
+    store_tile<D / 32, false, SLICE>(acc, sc, slice, lane, N - k0w,
+                                     [&](int r) __attribute__((always_inline)) { return base + (size_t)r * D; });
   }
 }
 
@@ -658,16 +651,31 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   // copy of row N-1; their lse * log2(e) is +inf, so P = 0.
   bf16x8 qf[D / 16], dof[D / 16];
   float Dq, lse2;  // -D and lse * log2(e) of this lane's query
-  {
-    const size_t qr = (size_t)min(qi, N - 1) * D + 8 * h2;
-    u32x4 of[D / 16];
+  const size_t qr = (size_t)min(qi, N - 1) * D + 8 * h2;
+  u32x4 of[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.q + head + qr + 16 * kk));
-      dof[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.dO + head + qr + 16 * kk));
-      of[kk] = ld_global16(p.o + head + qr + 16 * kk);
-    }
-    const float l = qi < N ? p.lse[(size_t)bh * N + qi] : -INFINITY;
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.q + head + qr + 16 * kk));
+    dof[kk] = __builtin_bit_cast(bf16x8, ld_global16(p.dO + head + qr + 16 * kk));
+    of[kk] = ld_global16(p.o + head + qr + 16 * kk);
+  }
+  const float lrow = qi < N ? p.lse[(size_t)bh * N + qi] : -INFINITY;
+
+  // K and V of this head as buffer resources: tail rows past N read as zero
+  // (and are masked).
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const TileDMA<D, BN> cp(w, lane);
+  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
+    cp.copy(p.k + head, head_bytes, j * BN * D * 2, kdst, w);
+    cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
+  };
+
+  // The first key tile's copy is issued before the row terms below wait
+  // for O and dO, so both round trips to memory overlap.
+  int jc = next_tile(0);
+  if (jc < kt_end) dma_kv(jc, kst[0], vst[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  {
     // D = rowsum(dO o O): this lane holds half of its row's elements, the
     // lane 32 apart the other half. With dropout dP is kept in units of
     // 1 - p, and so is D.
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     }
     acc = xhalf_sum(acc);
     Dq = qi < N ? -acc * p.dfac : 0.f;
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    lse2 = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
     // The dK/dV pass reads both from the workspace, padded to whole query
     // tiles per head (rows past N: -D = 0, lse * log2(e) = +inf).
     if (h2 == 0) {
@@ -696,15 +704,6 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
-
-  // K and V of this head as buffer resources: tail rows past N read as zero
-  // (and are masked).
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const TileDMA<D, BN> cp(w, lane);
-  auto dma_kv = [&](int j, FA_LDS uint8_t* kdst, FA_LDS uint8_t* vdst) __attribute__((always_inline)) {
-    cp.copy(p.k + head, head_bytes, j * BN * D * 2, kdst, w);
-    cp.copy(p.v + head, head_bytes, j * BN * D * 2, vdst, w);
-  };
 
   const float c = p.c;
   // Per-lane LDS offsets, computed once and opaque to the compiler (stage and
@@ -792,9 +791,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     }
   };
 
-  int jc = next_tile(0);
+  int pl = 0;  // LDS stage of the last tile (stage 1 - pl is free afterwards)
   if (jc < kt_end) {
-    dma_kv(jc, kst[0], vst[0]);
     wait_vmem();
     __syncthreads();
     auto step = [&](auto parity) __attribute__((always_inline)) -> bool {
@@ -814,23 +812,24 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
         __syncthreads();
       }
       jc = jn;
+      pl = P;
       return jn < kt_end;
     };
     while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
     }
   }
 
-  if (qi < N) {
-    uint16_t* dqr = p.dq + head + (size_t)qi * D;
-    const float sc = p.scale * (DROP ? p.drop.scale : 1.0f);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * dt + 8 * rg + 4 * h2;
-        *reinterpret_cast<u32x2*>(dqr + d0) = pack4_bf16(dqt[dt][4 * rg] * sc, dqt[dt][4 * rg + 1] * sc,
-                                                         dqt[dt][4 * rg + 2] * sc, dqt[dt][4 * rg + 3] * sc);
-      }
+  // dQ goes out through this wave's slice of the LDS stage that held the tile
+  // before the last (no wave reads it any more, and no copy targets it).
+  {
+    constexpr int SLICE = 2 * TILEB / 4;
+    constexpr int PER = TILEB / SLICE;  // slices per stage buffer
+    FA_LDS uint8_t* const kfree = pl ? (FA_LDS uint8_t*)k0_raw : (FA_LDS uint8_t*)k1_raw;
+    FA_LDS uint8_t* const vfree = pl ? (FA_LDS uint8_t*)v0_raw : (FA_LDS uint8_t*)v1_raw;
+    FA_LDS uint8_t* const slice = (w < PER ? kfree : vfree) + (w % PER) * SLICE;
+    uint16_t* const qbase = p.dq + head + (size_t)q0 * D;
+    store_tile<D / 32, false, SLICE>(dqt, p.scale * (DROP ? p.drop.scale : 1.0f), slice, lane, N - q0,
+                                     [&](int r) __attribute__((always_inline)) { return qbase + (size_t)r * D; });
   }
 }
 

@@ -89,6 +89,56 @@ __device__ __forceinline__ u32x2 pack4_bf16(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// Stores a wave's tile of MFMA results to global memory as bf16 rows, staged
+// through LDS. Written straight from the C/D layout, each store instruction
+// puts 8 bytes into each of 32 different rows, one memory request per row
+// segment; read back from LDS in row order, each instruction writes whole
+// 16-byte chunks of a few consecutive rows (16 times fewer segments for a
+// 32 x 128 tile).
+//   The tile is NB result blocks acc[b] (C/D layout above; the value of lane
+// l, index r sits in column x = 8*(r/4) + 4*(l/32) + r%4 of the block's
+// 32 x 32 and row l % 32). BY_BLOCK = false: block b holds tile columns
+// 32b + x of the 32 tile rows l % 32. BY_BLOCK = true: block b holds tile
+// rows 32b + l % 32 of the 32 tile columns x. Every value is multiplied by
+// `scale` (per lane) and rounded to bf16. buf is this wave's LDS slice of
+// SLICE bytes, touched by no other wave meanwhile; the tile passes through it
+// in as many column passes as it needs (chunk c of row r is stored at chunk
+// c ^ (r mod chunks per row), so the 8-byte writes and 16-byte reads of a
+// wave spread over the banks). Tile row r goes to rowp(r) (bf16 pointer of
+// its first column) when r < nrows.
+template <int NB, bool BY_BLOCK, int SLICE, typename RowPtr>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB], float scale, FA_LDS uint8_t* buf, int lane,
+                                           int nrows, RowPtr rowp) {
+  constexpr int PB = BY_BLOCK ? NB : (SLICE / 2048 < NB ? SLICE / 2048 : NB);  // blocks per pass
+  static_assert(PB >= 1 && NB % PB == 0 && (!BY_BLOCK || SLICE >= NB * 2048), "LDS slice too small");
+  constexpr int W = BY_BLOCK ? 32 : 32 * PB;  // tile columns per pass
+  constexpr int R = BY_BLOCK ? 32 * NB : 32;  // tile rows
+  constexpr int NCH = W / 8;                  // 16-byte chunks per row
+  constexpr int ROWB = 2 * W;
+  constexpr int RPI = 1024 / ROWB;  // rows per 64-lane read of 16 bytes each
+  const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ps = 0; ps < NB / PB; ++ps) {
+#pragma unroll
+    for (int bb = 0; bb < PB; ++bb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int b = ps * PB + bb;
+        const int row = BY_BLOCK ? 32 * b + c : c;
+        const int ch = BY_BLOCK ? rg : 4 * bb + rg;
+        *reinterpret_cast<FA_LDS u32x2*>(buf + row * ROWB + ((ch ^ (row % NCH)) * 16) + 8 * h) =
+            pack4_bf16(acc[b][4 * rg] * scale, acc[b][4 * rg + 1] * scale, acc[b][4 * rg + 2] * scale,
+                       acc[b][4 * rg + 3] * scale);
+      }
+#pragma unroll
+    for (int it = 0; it < R / RPI; ++it) {
+      const int row = it * RPI + lane / NCH, ch = lane % NCH;
+      const u32x4 v = *reinterpret_cast<const FA_LDS u32x4*>(buf + row * ROWB + ((ch ^ (row % NCH)) * 16));
+      if (row < nrows) *reinterpret_cast<u32x4*>(rowp(row) + ps * W + ch * 8) = v;
+    }
+  }
+}
+
 // Logical workgroup index such that consecutive logical indices land on the
 // same XCD: the dispatcher hands consecutive hardware ids to XCDs round
 // robin, so hardware id i runs on XCD i % 8.

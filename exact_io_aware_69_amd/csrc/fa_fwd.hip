@@ -295,6 +295,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   };
 
   int jc = next_tile(0);
+  int pl = 0;  // LDS stage of the last tile (stage 1 - pl is free afterwards)
   if (jc < kt_end) {
     bool act = wave_active(jc);
     dma_kv(jc, kst[0], vst[0]);
@@ -327,28 +328,29 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
       }
       jc = jn;
       act = act_n;
+      pl = P;
       return jn < kt_end;
     };
     while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
     }
   }
 
-  // Epilogue: O = acc / l (deferred normalisation), lse = ln sum exp.
+  // Epilogue: O = acc / l (deferred normalisation), lse = ln sum exp. O goes
+  // out through this wave's slice of the LDS stage that held the tile before
+  // the last (no wave reads it any more, and no copy targets it).
   const float l_tot = xhalf_sum(l_run);
   const float inv = l_tot > 0.f ? (DROP ? p.drop.scale : 1.0f) / l_tot : 0.f;
-  if (qi < N) {
-    uint16_t* orow = p.o + head + (size_t)qi * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * dt + 8 * rg + 4 * h2;
-        *reinterpret_cast<u32x2*>(orow + d0) =
-            pack4_bf16(oacc[dt][4 * rg] * inv, oacc[dt][4 * rg + 1] * inv, oacc[dt][4 * rg + 2] * inv,
-                       oacc[dt][4 * rg + 3] * inv);
-      }
-    if (h2 == 0) p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  {
+    constexpr int SLICE = 2 * TILEB / WAVES;
+    constexpr int PER = TILEB / SLICE;  // slices per stage buffer
+    FA_LDS uint8_t* const kfree = pl ? (FA_LDS uint8_t*)k0_raw : (FA_LDS uint8_t*)k1_raw;
+    FA_LDS uint8_t* const vfree = pl ? (FA_LDS uint8_t*)v0_raw : (FA_LDS uint8_t*)v1_raw;
+    FA_LDS uint8_t* const slice = (w < PER ? kfree : vfree) + (w % PER) * SLICE;
+    uint16_t* const obase = p.o + head + (size_t)q0 * D;
+    store_tile<D / 32, false, SLICE>(oacc, inv, slice, lane, N - q0,
+                                     [&](int r) __attribute__((always_inline)) { return obase + (size_t)r * D; });
   }
+  if (qi < N && h2 == 0) p.lse[(size_t)bh * N + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
