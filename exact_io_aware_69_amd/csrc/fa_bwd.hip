@@ -692,12 +692,6 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     acc = xhalf_sum(acc);
     Dq = qi < N ? -acc * p.dfac : 0.f;
     lse2 = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
-    // The dK/dV pass reads both from the workspace, padded to whole query
-    // tiles per head (rows past N: -D = 0, lse * log2(e) = +inf).
-    if (h2 == 0) {
-      p.Dneg[(size_t)bh * p.Npad + qi] = Dq;
-      p.lse2[(size_t)bh * p.Npad + qi] = lse2;
-    }
   }
   f32x16 dqt[D / 32];
 #pragma unroll
@@ -819,6 +813,14 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(const BwdParams p) {
     }
   }
 
+  // The dK/dV pass reads -D and lse * log2(e) from the workspace, padded to
+  // whole query tiles per head (rows past N: -D = 0, lse * log2(e) = +inf).
+  // Stored only now: the tile loop's waits for its copies count stores too,
+  // so stores issued before it would hold up the first tile.
+  if (h2 == 0) {
+    p.Dneg[(size_t)bh * p.Npad + qi] = Dq;
+    p.lse2[(size_t)bh * p.Npad + qi] = lse2;
+  }
   // dQ goes out through this wave's slice of the LDS stage that held the tile
   // before the last (no wave reads it any more, and no copy targets it).
   {
