@@ -560,7 +560,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                    "block_sparse": cfg["sparse"], "pass": "fwd+bwd" if cfg["bwd"] else "fwd",
                    "seed": args.seed, "parallelism": "single GPU",
-                   "fwd_tiles": list(tiles) if tiles else [128, 64],
+                   "fwd_tiles": list(tiles) if tiles else list(_lib.fa_tile_config(0, d, causal)[1:]),
                    **({"fa1_seq_groups": args.fa1_seq_groups} if args.fa1 else {}),
                    **({"dropout_p": args.dropout} if drop else {}),
                    "impl": ("standard (materialised S)" if args.standard else

@@ -78,10 +78,11 @@ int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* dr) {
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
              int causal, float scale, const uint8_t* mask, bool sparse, uint8_t* visited, void* stream,
-             int bm = fa::FWD_BM, int bn = fa::FWD_BN, const fa::Dropout* drop = nullptr) {
+             int bm = fa::FWD_BM, int bn = 0, const fa::Dropout* drop = nullptr) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale);
   if (st != FA_OK) return st;
+  if (bn == 0) bn = d == 128 ? fa::fwd_bn<128>() : fa::fwd_bn<64>();  // the default tiles
   if (sparse && !mask) return FA_ERR_MASK;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
   fa::FwdParams p;
@@ -309,7 +310,7 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   const int st = make_dropout(dropout_p, seed, offset, &dr);
   if (st != FA_OK) return st;
   return fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, block_mask, block_mask != nullptr, nullptr, stream,
-                  fa::FWD_BM, fa::FWD_BN, &dr);
+                  fa::FWD_BM, 0, &dr);
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
@@ -353,7 +354,7 @@ int fa_tile_config(int pass, int d, int causal, int* bm, int* bn) {
   if (!bm || !bn) return FA_ERR_NULL;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
   switch (pass) {
-    case 0: *bm = fa::FWD_BM; *bn = fa::FWD_BN; return FA_OK;
+    case 0: *bm = fa::FWD_BM; *bn = d == 128 ? fa::fwd_bn<128>() : fa::fwd_bn<64>(); return FA_OK;
     case 1:
       *bm = d == 128 ? fa::bwd_kv_bm<128>() : fa::bwd_kv_bm<64>();
       *bn = d == 128 ? fa::bwd_kv_bn<128>() : fa::bwd_kv_bn<64>();

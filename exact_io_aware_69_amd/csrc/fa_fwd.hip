@@ -41,8 +41,12 @@
 namespace fa {
 
 template <int D, int BN, int WAVES, bool CAUSAL, bool SPARSE, bool DEBUG, bool DROP = false>
-// Two 4-wave workgroups per CU unless the two K/V stages of one exceed half the LDS.
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 : 1) void fa_fwd_kernel(const FwdParams p) {
+// Two 4-wave workgroups per CU unless the two K/V stages of one exceed half
+// the LDS; three at d = 128 with 32-key tiles (not with dropout, whose
+// generator needs more registers).
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && D == 128 && BN == 32 && !DROP) ? 3
+                                         : (WAVES == 4 && BN * D <= 64 * 128)          ? 2
+                                                                                       : 1) void fa_fwd_kernel(const FwdParams p) {
   constexpr int BM = 32 * WAVES;  // query rows per workgroup
   static_assert(MASK_BLOCK % BN == 0 && BM <= 2 * MASK_BLOCK, "a tile spans at most one mask column, two mask rows");
   constexpr int TILEB = BN * D * 2;
@@ -54,8 +58,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && BN * D <= 64 * 128) ? 2 
   // LDS reads issued ahead of their products (below). Not in the lazy d = 64
   // configuration (they gained nothing at d = 64, and their registers would
   // cost it the fourth wave per SIMD), nor in the 8-wave d = 128, 128-key
-  // configuration, which has no registers left for them.
-  constexpr bool AHEAD = !LAZY_MAX && !(D == 128 && BN == 128 && WAVES == 8);
+  // configuration, which has no registers left for them, nor in the d = 128,
+  // 32-key one, whose third workgroup per CU leaves 168 registers a wave.
+  constexpr bool AHEAD = !LAZY_MAX && !(D == 128 && BN == 128 && WAVES == 8) &&
+                         !(D == 128 && BN == 32 && WAVES == 4 && !DROP);
   constexpr float SUM_MAX = 256.0f;  // largest probability allowed against the reference (2^TAU)
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   // Two LDS stages for K and two for V, as four separate objects: the stage
@@ -391,7 +397,7 @@ bool fwd_config_supported(int bm, int bn) {
 template <int D>
 hipError_t launch_fwd_d(const FwdParams& p, int BH, int bm, int bn, bool causal, bool sparse, bool debug,
                         hipStream_t st) {
-  if (debug) return launch_fwd_c<D, FWD_BN, FWD_BM / 32>(p, BH, causal, sparse, true, st);
+  if (debug) return launch_fwd_c<D, fwd_bn<D>(), FWD_BM / 32>(p, BH, causal, sparse, true, st);
   if (bm == 128 && bn == 32) return launch_fwd_c<D, 32, 4>(p, BH, causal, sparse, false, st);
   if (bm == 128 && bn == 64) return launch_fwd_c<D, 64, 4>(p, BH, causal, sparse, false, st);
   if (bm == 128 && bn == 128) return launch_fwd_c<D, 128, 4>(p, BH, causal, sparse, false, st);
@@ -411,10 +417,10 @@ template <int D>
 hipError_t launch_fwd_dropout_d(const FwdParams& p, int BH, bool causal, bool sparse, hipStream_t st) {
   constexpr int W = FWD_BM / 32;
   if (causal)
-    return sparse ? launch_fwd_t<D, FWD_BN, W, true, true, false, true>(p, BH, st)
-                  : launch_fwd_t<D, FWD_BN, W, true, false, false, true>(p, BH, st);
-  return sparse ? launch_fwd_t<D, FWD_BN, W, false, true, false, true>(p, BH, st)
-                : launch_fwd_t<D, FWD_BN, W, false, false, false, true>(p, BH, st);
+    return sparse ? launch_fwd_t<D, fwd_bn<D>(), W, true, true, false, true>(p, BH, st)
+                  : launch_fwd_t<D, fwd_bn<D>(), W, true, false, false, true>(p, BH, st);
+  return sparse ? launch_fwd_t<D, fwd_bn<D>(), W, false, true, false, true>(p, BH, st)
+                : launch_fwd_t<D, fwd_bn<D>(), W, false, false, false, true>(p, BH, st);
 }
 
 hipError_t launch_fwd_dropout(const FwdParams& p, int BH, int d, bool causal, bool sparse, hipStream_t st) {

@@ -8,9 +8,15 @@
 namespace fa {
 
 // Forward: 4 waves per workgroup, 32 query rows per wave (the waves split
-// the query rows of the tile, never the keys), key/value tiles of FWD_BN rows.
+// the query rows of the tile, never the keys), key/value tiles of fwd_bn<D>()
+// rows. At d = 128, 32-key tiles let three workgroups share a CU (32 KiB of
+// LDS and at most 168 registers each), which measured faster than two with
+// 64-key tiles; d = 64 keeps 64-key tiles at four workgroups per CU. The
+// dropout forward uses the same tiles (two workgroups per CU at d = 128),
+// so that with p = 0 it gives the plain forward's results bit for bit.
 constexpr int FWD_BM = 128;
-constexpr int FWD_BN = 64;
+template <int D>
+constexpr int fwd_bn() { return D == 128 ? 32 : 64; }
 // Backward dK/dV kernel: a workgroup owns bwd_kv_bn<D>() keys, one P-wave
 // and one dS-wave per 32 keys (one computes P and dV, the other dP, dS and
 // dK); query tiles of bwd_kv_bm<D>() rows stream through LDS. d = 128: 128

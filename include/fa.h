@@ -90,7 +90,8 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
  *       256: 8 waves, one workgroup per CU),
  *   bn: keys per K/V tile staged in LDS.
  * Supported (bm, bn): (128, 32), (128, 64), (128, 128), (256, 64),
- * (256, 128); any other pair returns FA_ERR_SHAPE. fa_fwd uses (128, 64). */
+ * (256, 128); any other pair returns FA_ERR_SHAPE. fa_fwd and
+ * fa_fwd_dropout use (128, 32) at d = 128 and (128, 64) at d = 64. */
 int fa_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float scale,
                  const uint8_t* block_mask, int bm, int bn, void* stream);
@@ -246,10 +247,10 @@ int fa_dropout_keep(int B, int H, int N, float dropout_p, uint64_t seed,
  * A utility of this library: no passage of the pages defines it (they fix
  * no tile sizes). Returns FA_ERR_UNSUPPORTED_D for d not in {64, 128},
  * FA_ERR_SHAPE for a pass outside 0..2, FA_ERR_NULL for a NULL output.
- * pass: 0 = forward, 1 = backward dK/dV kernel, 2 = backward dQ kernel;
- * causal: nonzero for the causal kernels (the d = 128 dQ kernel streams
- * 64-key tiles when causal, 32-key tiles otherwise). bm = query rows per
- * tile, bn = key rows per tile. */
+ * pass: 0 = forward (every forward entry point but fa_fwd_tiles), 1 =
+ * backward dK/dV kernel, 2 = backward dQ kernel; causal: nonzero for the causal kernels
+ * (the d = 128 dQ kernel streams 64-key tiles when causal, 32-key tiles
+ * otherwise). bm = query rows per tile, bn = key rows per tile. */
 int fa_tile_config(int pass, int d, int causal, int* bm, int* bn);
 
 /* Debug forward: same computation as fa_fwd_blocksparse (block_mask may be
