@@ -36,8 +36,10 @@ def group_size(wgs_per_cu, cus_per_xcd, BH, ntile):
         return 1
     hx = BH // 8
     g = 1
-    while g < hx and (g * ntile < 2 * wgs_per_cu * cus_per_xcd or hx % g):
+    while g < hx and g < 16 and (g * ntile < 2 * wgs_per_cu * cus_per_xcd or hx % g):
         g += 1
+    while hx % g:
+        g -= 1
     return g
 
 
