@@ -24,8 +24,9 @@
 //     register staging), two LDS stages each, one barrier per tile: the next
 //     tile's copy is in flight while the current one is consumed.
 //   * Vector-ALU work per score is one FMA, one exp2 and one add, plus a
-//     share of max3 and bf16 packing; two waves per SIMD overlap one wave's
-//     exponentials with the other's MFMAs.
+//     share of max3 and bf16 packing; the other waves of a SIMD (three
+//     workgroups per CU at d = 128 with 32-key tiles, up to four at d = 64)
+//     run their MFMAs while one wave takes its exponentials.
 //   * The reference max used in the exponent is only moved when a row max
 //     grows by more than 2^8 (in the exp2 domain); until then the
 //     accumulator is not rescaled. The result is unchanged because O and l
@@ -59,9 +60,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && D == 128 && BN == 32 && 
   // configuration (they gained nothing at d = 64, and their registers would
   // cost it the fourth wave per SIMD), nor in the 8-wave d = 128, 128-key
   // configuration, which has no registers left for them, nor in the d = 128,
-  // 32-key one, whose third workgroup per CU leaves 168 registers a wave.
+  // 32-key one, whose third workgroup per CU leaves 168 registers a wave:
+  // there only the K reads go ahead (KAHEAD k-steps; its registers peak in
+  // the P V phase, not in the score products).
   constexpr bool AHEAD = !LAZY_MAX && !(D == 128 && BN == 128 && WAVES == 8) &&
                          !(D == 128 && BN == 32 && WAVES == 4 && !DROP);
+  constexpr bool AHEAD_K = AHEAD || (D == 128 && BN == 32 && WAVES == 4 && !DROP);
+  constexpr int KAHEAD = AHEAD ? 2 : 3;
   constexpr float SUM_MAX = 256.0f;  // largest probability allowed against the reference (2^TAU)
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   // Two LDS stages for K and two for V, as four separate objects: the stage
@@ -163,16 +168,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 && D == 128 && BN == 32 && 
 #pragma unroll
       for (int mt = 0; mt < NS; ++mt)
         s[mt] = mfma32(ld_lds16(ks + 32 * mt * D * 2, kofs[kk]), qf[kk], s[mt]);
-    // Issue order: the K reads of the first two k-steps, then each k-step's
-    // products followed by the reads two k-steps ahead.
-    if constexpr (AHEAD) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NS, 0);
+    // Issue order: the K reads of the first KAHEAD k-steps, then each
+    // k-step's products followed by the reads KAHEAD k-steps ahead.
+    if constexpr (AHEAD_K) {
+      __builtin_amdgcn_sched_group_barrier(0x100, KAHEAD * NS, 0);
 #pragma unroll
-      for (int kk = 0; kk < D / 16 - 2; ++kk) {
+      for (int kk = 0; kk < D / 16 - KAHEAD; ++kk) {
         __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, NS, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KAHEAD * NS, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
