@@ -892,7 +892,9 @@ hipError_t launch_bwd_t(const BwdParams& p, int BH, int stages, hipStream_t st) 
     const auto kernel = fa_bwd_dkdv_kernel<D, CAUSAL, SPARSE, DEBUG, DROP>;
     static const int wgs = wgs_per_cu((const void*)kernel, 64 * bwd_kv_waves<D>());
     BwdParams q = p;
-    q.hgrp = INTERLEAVE ? head_group(wgs, cus_per_xcd(), BH, slots) : 1;
+    // Dense causal: a wider group (see head_group); block-sparse: the default.
+    q.hgrp = !INTERLEAVE ? 1 : SPARSE ? head_group(wgs, cus_per_xcd(), BH, slots)
+                                      : head_group(wgs, cus_per_xcd(), BH, slots, 8, 8);
     hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * slots)), dim3(64 * bwd_kv_waves<D>()), 0, st, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -149,21 +149,26 @@ inline int cus_per_xcd() {
 // the XCD idles while they finish; interleaving G heads rank by rank starts
 // the heavy tiles of G heads together. Too large a G spreads the XCD's
 // slots over more heads at once and lowers the L2 reuse of each head's K/V
-// (or Q/dO). G is the smallest divisor of BH / 8 with G * ntile >= 2 *
-// slots (1 when 8 does not divide BH): measured on causal d = 64 and 128
-// shapes, it was as fast as or faster than both G = 1 and G = BH / 8. It is
-// capped at the largest divisor of BH / 8 not above kMaxHeadGroup: short
+// (or Q/dO). G is the smallest divisor of BH / 8 with G * ntile >= cover *
+// slots (1 when 8 does not divide BH). With cover = 2 (forward, dQ and the
+// block-sparse dK/dV) it was as fast as or faster than both G = 1 and
+// G = BH / 8 on causal d = 64 and 128 shapes. The dense causal dK/dV launch
+// (one long workgroup per CU) takes cover = 8 with the cap at 8: 1-3% faster
+// from N = 4096 to 16384 and up to 3.6% at N = 512, not slower anywhere
+// measured (d = 64 and 128, N = 512 to 16384). G is capped at the largest
+// divisor of BH / 8 not above `cap` (default kMaxHeadGroup): short
 // sequences have few tiles per head, and at N = 512 (ntile 4) the uncapped
 // rule picked G = 64, 10-17% slower than 16 in the forward and dK/dV passes
 // of causal d = 64 and 128 launches; at N = 1024 the two choices were within
 // a few percent either way, and from N = 2048 the cap does not bind.
 constexpr int kMaxHeadGroup = 16;
-inline int head_group(int wgs_per_cu, int cus_per_xcd, int BH, int ntile) {
+inline int head_group(int wgs_per_cu, int cus_per_xcd, int BH, int ntile, int cover = 2,
+                      int cap = kMaxHeadGroup) {
   if (BH % 8 != 0 || ntile < 1) return 1;
   const int hx = BH / 8;
   const int slots = wgs_per_cu * cus_per_xcd;
   int g = 1;
-  while (g < hx && g < kMaxHeadGroup && (g * ntile < 2 * slots || hx % g != 0)) ++g;
+  while (g < hx && g < cap && (g * ntile < cover * slots || hx % g != 0)) ++g;
   while (hx % g != 0) --g;  // largest divisor of hx not above the cap
   return g;
 }

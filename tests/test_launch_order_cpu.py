@@ -50,23 +50,30 @@ int main() {
     }
   }
   // head_group: 1 unless 8 divides BH; otherwise the smallest divisor of
-  // BH / 8 with G * ntile >= 2 * slots, or BH / 8 when none reaches it,
-  // capped at the largest divisor of BH / 8 not above kMaxHeadGroup.
-  for (int BH : {1, 4, 8, 12, 16, 32, 64, 128, 256}) {
-    for (int ntile : {1, 16, 32, 64, 128, 512}) {
-      for (int wgs : {1, 2, 3, 4}) {
-        const int cus = 32, slots = wgs * cus;
-        const int G = fa::head_group(wgs, cus, BH, ntile);
-        if (BH % 8) { CHECK(G == 1, "not /8 BH=%d G=%d", BH, G); continue; }
-        const int hx = BH / 8;
-        CHECK(G >= 1 && hx % G == 0, "divisor BH=%d ntile=%d wgs=%d G=%d", BH, ntile, wgs, G);
-        int cap = 1;  // largest divisor of hx not above the cap
-        for (int g = 1; g <= fa::kMaxHeadGroup && g <= hx; ++g)
-          if (hx % g == 0) cap = g;
-        CHECK(G <= cap, "cap BH=%d ntile=%d wgs=%d G=%d", BH, ntile, wgs, G);
-        CHECK(G == hx || G == cap || G * ntile >= 2 * slots, "cover BH=%d ntile=%d wgs=%d G=%d", BH, ntile, wgs, G);
-        for (int g = 1; g < G; ++g)
-          CHECK(hx % g != 0 || g * ntile < 2 * slots, "minimal BH=%d ntile=%d wgs=%d G=%d g=%d", BH, ntile, wgs, G, g);
+  // BH / 8 with G * ntile >= cover * slots, or BH / 8 when none reaches it,
+  // capped at the largest divisor of BH / 8 not above `cap`. Checked for the
+  // default (cover 2, cap kMaxHeadGroup) and the dense causal dK/dV setting
+  // (cover 8, cap 8).
+  for (int mode = 0; mode < 2; ++mode) {
+    const int cover = mode ? 8 : 2, capv = mode ? 8 : fa::kMaxHeadGroup;
+    for (int BH : {1, 4, 8, 12, 16, 32, 64, 128, 256}) {
+      for (int ntile : {1, 16, 32, 64, 128, 512}) {
+        for (int wgs : {1, 2, 3, 4}) {
+          const int cus = 32, slots = wgs * cus;
+          const int G = mode ? fa::head_group(wgs, cus, BH, ntile, cover, capv) : fa::head_group(wgs, cus, BH, ntile);
+          if (BH % 8) { CHECK(G == 1, "not /8 BH=%d G=%d", BH, G); continue; }
+          const int hx = BH / 8;
+          CHECK(G >= 1 && hx % G == 0, "divisor BH=%d ntile=%d wgs=%d G=%d", BH, ntile, wgs, G);
+          int cap = 1;  // largest divisor of hx not above the cap
+          for (int g = 1; g <= capv && g <= hx; ++g)
+            if (hx % g == 0) cap = g;
+          CHECK(G <= cap, "cap BH=%d ntile=%d wgs=%d G=%d mode=%d", BH, ntile, wgs, G, mode);
+          CHECK(G == hx || G == cap || G * ntile >= cover * slots, "cover BH=%d ntile=%d wgs=%d G=%d mode=%d", BH, ntile,
+                wgs, G, mode);
+          for (int g = 1; g < G; ++g)
+            CHECK(hx % g != 0 || g * ntile < cover * slots, "minimal BH=%d ntile=%d wgs=%d G=%d g=%d mode=%d", BH, ntile,
+                  wgs, G, g, mode);
+        }
       }
     }
   }

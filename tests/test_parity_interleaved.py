@@ -29,14 +29,14 @@ CASES = [
 ]
 
 
-def group_size(wgs_per_cu, cus_per_xcd, BH, ntile):
+def group_size(wgs_per_cu, cus_per_xcd, BH, ntile, cover=2, cap=16):
     """The group rule stated in fa_params.h (head_group), for the assertion
     below that these shapes interleave heads."""
     if BH % 8 or ntile < 1:
         return 1
     hx = BH // 8
     g = 1
-    while g < hx and g < 16 and (g * ntile < 2 * wgs_per_cu * cus_per_xcd or hx % g):
+    while g < hx and g < cap and (g * ntile < cover * wgs_per_cu * cus_per_xcd or hx % g):
         g += 1
     while hx % g:
         g -= 1
@@ -52,6 +52,7 @@ def test_interleaved_whole_outputs(case):
     # 2 * 32 CUs * (1..4 workgroups per CU): G = B*H/8 = 2 for every kernel.
     for wgs in (1, 2, 3, 4):
         assert group_size(wgs, 32, B * H, -(-N // 32)) == 2
+        assert group_size(wgs, 32, B * H, -(-N // 32), cover=8, cap=8) == 2  # dense causal dK/dV
     inp = make_inputs(41, B, H, N, d, sparse=sparse, p=0.3)
     mask = inp.get("mask")
     m = None if mask is None else torch.from_numpy(mask).to("cuda:0")
